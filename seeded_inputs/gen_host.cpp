@@ -1,0 +1,72 @@
+/*
+ * gen_host.cpp -- host build of the seeded input generator (zs_gen.h).
+ * Fills host arrays with windows [i0, i0+n) of a keyed tensor.  Threads
+ * split the window into contiguous pieces; every element depends only on
+ * its key and index, so the thread count does not change the values.
+ */
+#include <thread>
+#include <vector>
+
+#include "zs_gen.h"
+
+namespace {
+
+template <class F>
+void parallel(int64_t n, int threads, F body) {
+  if (threads < 1) threads = 1;
+  const int64_t min_piece = 1 << 16;
+  if (n < min_piece * 2 || threads == 1) {
+    body(0, n);
+    return;
+  }
+  if (threads > n / min_piece) threads = int(n / min_piece);
+  std::vector<std::thread> pool;
+  const int64_t piece = (n + threads - 1) / threads;
+  for (int w = 0; w < threads; ++w) {
+    const int64_t lo = w * piece;
+    const int64_t hi = lo + piece < n ? lo + piece : n;
+    if (lo >= hi) break;
+    pool.emplace_back([=] { body(lo, hi); });
+  }
+  for (auto &t : pool) t.join();
+}
+
+}  // namespace
+
+extern "C" {
+
+uint64_t zsg_host_key(uint64_t seed, uint32_t tid, uint32_t step, uint32_t rank) {
+  return zsg_key(seed, tid, step, rank);
+}
+
+void zsg_host_fill_f32(float *out, int64_t n, uint64_t seed, uint32_t tid,
+                       uint32_t step, uint32_t rank, int64_t i0, float sigma,
+                       int outliers, int kind, int threads) {
+  const uint64_t h = zsg_key(seed, tid, step, rank);
+  parallel(n, threads, [=](int64_t lo, int64_t hi) {
+    for (int64_t j = lo; j < hi; ++j)
+      out[j] = zsg_value(h, uint64_t(i0 + j), sigma, outliers, kind);
+  });
+}
+
+void zsg_host_fill_bf16(uint16_t *out, int64_t n, uint64_t seed, uint32_t tid,
+                        uint32_t step, uint32_t rank, int64_t i0, float sigma,
+                        int outliers, int threads) {
+  const uint64_t h = zsg_key(seed, tid, step, rank);
+  parallel(n, threads, [=](int64_t lo, int64_t hi) {
+    for (int64_t j = lo; j < hi; ++j)
+      out[j] = zsg_to_bf16(zsg_value(h, uint64_t(i0 + j), sigma, outliers, ZSG_KIND_NORMAL));
+  });
+}
+
+/* Rows k = 0..n_d-1 of one step's gradient contributions, row k at
+ * out + k*row_stride, elements [i0, i0+n) of each rank's shard slice. */
+void zsg_host_fill_contrib(uint16_t *out, int32_t n_d, int64_t row_stride,
+                           int64_t n, uint64_t seed, uint32_t step, int64_t i0,
+                           float sigma, int outliers, int threads) {
+  for (int32_t k = 0; k < n_d; ++k)
+    zsg_host_fill_bf16(out + k * row_stride, n, seed, ZSG_GRAD, step, uint32_t(k),
+                       i0, sigma, outliers, threads);
+}
+
+}  // extern "C"

@@ -1,0 +1,392 @@
+"""Pins of the CPU oracle to facts fixed outside it.
+
+Each test checks one oracle routine against something it cannot simply
+restate: numbers the pages print, closed forms of the mathematics, exact
+rational arithmetic, exhaustive enumeration, or hand-worked tables.  Each is
+chosen so that a plausible slip (a dropped term, a wrong sign, an off-by-one
+step counter, a transposed operand, a wrong rounding direction) fails it.
+"""
+
+from __future__ import annotations
+
+import json
+import os
+import subprocess
+import tempfile
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle as O
+import seeded_inputs as S
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _bf16_bits(values) -> np.ndarray:
+    """bf16 patterns of values that are exactly representable in bf16."""
+    f = np.asarray(values, dtype=np.float32)
+    u = f.view(np.uint32)
+    assert np.all((u & 0xFFFF) == 0), "value not exact in bf16"
+    return (u >> 16).astype(np.uint16)
+
+
+def _bf16_to_float(bits: np.ndarray) -> np.ndarray:
+    return (bits.astype(np.uint32) << 16).view(np.float32)
+
+
+# ------------------------------------------------------------- memory model
+
+def test_memory_model_printed_values():
+    g = json.load(open(os.path.join(GOLDEN, "memory_model.json")))
+    for c in g["cases"]:
+        got = O.model_state_bytes(c["psi"], c["n_d"], c["stage"]) / 1e9
+        assert round(got, c["digits"]) == c["gb"], c["source"]
+    # GPT-2 1.5B: at least 24 GB of model states against 3 GB of
+    # half-precision weights, a ratio of (2+2+K)/2 = 8
+    hw = g["half_weights"]
+    assert O.model_state_bytes(hw["psi"], 1, 0) / 1e9 / hw["gb"] == 8.0
+
+
+def test_memory_model_limits_and_consistency():
+    lim = json.load(open(os.path.join(GOLDEN, "memory_model.json")))["limits"]
+    psi = 1e9
+    base = O.model_state_bytes(psi, 1, 0)
+    assert base == 16 * psi
+    big = 1e9  # N_d -> infinity
+    assert abs(base / O.model_state_bytes(psi, big, 1) - lim["stage1"]) < 1e-6
+    assert abs(base / O.model_state_bytes(psi, big, 2) - lim["stage2"]) < 1e-6
+    for nd in (2, 8, 64, 1024):
+        assert base / O.model_state_bytes(psi, nd, 3) == pytest.approx(nd, rel=1e-12)
+        # every stage is bounded by the one before it
+        s = [O.model_state_bytes(psi, nd, k) for k in range(4)]
+        assert s[0] > s[1] > s[2] > s[3]
+    # with one GPU every stage is plain data parallelism
+    for k in range(4):
+        assert O.model_state_bytes(psi, 1, k) == base
+
+
+# ---------------------------------------------------------------- bf16 cast
+
+def test_bf16_round_exhaustive():
+    """All 2^32 binary32 patterns against a nearest-neighbour definition."""
+    src = os.path.join(ROOT, "tests", "native", "bf16_exhaustive.c")
+    so = os.path.join(ROOT, "oracle", "libzsoracle.so")
+    with tempfile.TemporaryDirectory() as d:
+        exe = os.path.join(d, "bf16ex")
+        subprocess.run(["gcc", "-O2", src, so, f"-Wl,-rpath,{os.path.dirname(so)}", "-lm",
+                        "-pthread", "-o", exe], check=True)
+        r = subprocess.run([exe], capture_output=True, text=True, timeout=600)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "mismatches 0" in r.stdout
+
+
+def test_fp32_master_keeps_small_updates():
+    """fp32 master weights exist so that small updates do not vanish
+    ("Memory Consumption Analysis": optimizer state in fp32 so that tiny
+    updates do not underflow; "精度混合训练": the fp32 parameter is the final
+    output).  theta = 1 with |step| ~ 1e-4, far below half a bf16 ulp at 1
+    (2^-8): a bf16-only weight never moves, the fp32 master moves every step
+    and its bf16 copy changes once the drift passes 2^-8 (rounded)."""
+    n = 1
+    rows = [_bf16_bits([1.0])]                   # constant gradient g = 1
+    h = O.Hyper(lr=1e-4, beta1=0.9, beta2=0.999, eps=1e-8)
+    master = np.ones(n, np.float32)
+    m = np.zeros(n, np.float32)
+    v = np.zeros(n, np.float32)
+    bf16_only = np.float32(1.0)
+    seen = []
+    for t in range(1, 31):
+        h.t = t
+        out = O.step(rows, master, m, v, h)
+        seen.append((float(master[0]), int(out.p[0])))
+        # a bf16-only update: round(1 - 1e-4) in bf16 is 1 again
+        bf16_only = _bf16_to_float(O.f32_to_bf16(np.array([bf16_only - np.float32(1e-4)])))[0]
+    assert bf16_only == 1.0
+    # constant g from zero state: every step is lr*g/(|g|+eps) ~ 1e-4
+    assert seen[9][0] == pytest.approx(1 - 10 * 1e-4, abs=1e-6)
+    assert seen[9][1] == 0x3F80                   # bf16 copy still reads 1.0
+    # 1 - k*1e-4 rounds to bf16 1 - 2^-8 once k*1e-4 > 2^-9 (k >= 20)
+    first = next(t for t, (_, p) in enumerate(seen, 1) if p != 0x3F80)
+    assert first == 20
+    assert seen[first - 1][1] == 0x3F7F           # 0.99609375 = 1 - 2^-8
+
+
+# ------------------------------------------------------- a1 reduce + average
+
+def test_reduce_average_least_squares_identity():
+    """The mean of per-rank gradients equals the full-batch gradient
+    ("How Standard Data Parallelism Works": the full-data gradient is the
+    average of the subset gradients).  Linear least squares
+    L(theta) = 1/(2B) ||X theta - y||^2 with X in {-1,0,1}, small integer y and
+    theta, B = N_d * b with b a power of two: every per-rank gradient
+    (1/b) X_r^T (X_r theta - y_r) is a dyadic number with <= 8 significant
+    bits (exact in bf16), so the oracle's average must equal the full-batch
+    gradient (1/B) X^T (X theta - y), computed exactly, bit for bit."""
+    rng = np.random.default_rng(7)
+    for nd, b, d in [(4, 4, 16), (8, 2, 32), (16, 4, 24), (64, 1, 24)]:
+        B = nd * b
+        X = rng.integers(-1, 2, size=(B, d))
+        theta = rng.integers(-2, 3, size=d)
+        y = rng.integers(-3, 4, size=B)
+        resid = X @ theta - y
+        rows = []
+        for r in range(nd):
+            sl = slice(r * b, (r + 1) * b)
+            gr = [Fraction(int(x), b) for x in X[sl].T @ resid[sl]]
+            rows.append(_bf16_bits([float(x) for x in gr]))
+        full = [Fraction(int(x), B) for x in X.T @ resid]
+        got = O.reduce_average(rows)
+        assert [Fraction(float(x)) for x in got] == full, (nd, b, d)
+
+
+def test_reduce_sum_exact_audit():
+    """The fp64 rank-order sum is the exact sum of the bf16 contributions
+    (exact rationals) on seeded draws, outliers included."""
+    w = S.by_name("gpt2-small-flat")
+    for i0 in (0, 1_000_003, w.shard_len - 4096):
+        rows = S.host_contrib(w, 1, i0, 4096)
+        s = O.reduce_sum(list(rows))
+        vals = _bf16_to_float(rows)
+        for i in range(0, 4096, 7):
+            exact = sum(Fraction(float(vals[k, i])) for k in range(w.n_d))
+            assert Fraction(float(s[i])) == exact
+        # and the average is that exact sum / N_d rounded once to binary32
+        gbar = O.reduce_average(list(rows))
+        assert np.array_equal(gbar, (s / w.n_d).astype(np.float32))
+
+
+def test_reduce_single_rank_is_conversion():
+    bits = S.host_bf16(10_000, 99, S.GRAD, 1, 0, 0, 1e-3)
+    assert np.array_equal(O.reduce_average([bits]), _bf16_to_float(bits))
+
+
+def test_reduce_uses_every_rank_in_place():
+    """Moving one unit between ranks keeps the mean; a unit in rank k shows
+    up in the mean as 1/N_d at its own index only (no index mix-up)."""
+    nd, n = 8, 64
+    for k in range(nd):
+        rows = [np.zeros(n, np.uint16) for _ in range(nd)]
+        rows[k][k * 3] = _bf16_bits([8.0])[0]
+        g = O.reduce_average(rows)
+        want = np.zeros(n, np.float32)
+        want[k * 3] = 1.0
+        assert np.array_equal(g, want)
+
+
+# ------------------------------------------------------------ a3 Adam forms
+
+def _adam_run(g_seq, theta0, h: O.Hyper, m0=None, v0=None):
+    n = len(theta0)
+    master = np.array(theta0, np.float32)
+    m = np.zeros(n, np.float32) if m0 is None else np.array(m0, np.float32)
+    v = np.zeros(n, np.float32) if v0 is None else np.array(v0, np.float32)
+    hist = []
+    for t, g in enumerate(g_seq, 1):
+        h.t = t
+        O.adam(master, m, v, np.asarray(g, np.float32), 1.0, h)
+        hist.append(master.copy())
+    return hist, m, v
+
+
+def test_adam_first_step_closed_form():
+    """From m = v = 0, bias-corrected Adam's first step is
+    -lr * g / (|g| + eps) whatever beta1, beta2 (m_hat = g, v_hat = g^2).
+    Includes gradients far below eps, where the step is ~ -lr g / eps."""
+    g = np.concatenate([S.host_f32(2000, 5, S.GRAD, 1, 0, 0, 1e-3),
+                        np.array([1e-12, -3e-10, 5e-9, 1e-8, -2e-8, 0.0, 0.25], np.float32)])
+    theta0 = S.host_f32(g.size, 5, S.MASTER, 0, 0, 0, 0.02)
+    for b1, b2, lr, eps in [(0.9, 0.999, 1e-3, 1e-8), (0.5, 0.95, 1e-4, 1e-6)]:
+        h = O.Hyper(lr=lr, beta1=b1, beta2=b2, eps=eps)
+        (th1,), _, _ = _adam_run([g], theta0, h)
+        lr64, eps64 = float(np.float32(lr)), float(np.float32(eps))
+        g64 = g.astype(np.float64)
+        want = theta0.astype(np.float64) - lr64 * g64 / (np.abs(g64) + eps64)
+        # the oracle rounds theta' once; m_hat, v_hat carry a few binary64 ulps
+        assert np.all(np.abs(th1 - want) <= np.spacing(np.abs(want).astype(np.float32)))
+
+
+def test_adam_constant_gradient_closed_form():
+    """Constant g from zero state: m_hat = g and v_hat = g^2 at every t (the
+    bias corrections undo the geometric sums exactly), so
+    theta_T = theta_0 - T lr g / (|g| + eps).  A wrong exponent in a bias
+    correction, or t off by one, breaks this from step 2 on."""
+    g = np.array([1e-3, -2e-4, 0.5, -7e-6, 3e-9], np.float32)
+    theta0 = np.zeros(g.size, np.float32)
+    h = O.Hyper(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8)
+    T = 25
+    hist, _, _ = _adam_run([g] * T, theta0, h)
+    lr, eps = float(np.float32(1e-3)), float(np.float32(1e-8))
+    g64 = g.astype(np.float64)
+    for t, th in enumerate(hist, 1):
+        want = -t * lr * g64 / (np.abs(g64) + eps)
+        # fp32 rounding of m, v and theta per step: a few ulps per step
+        assert np.allclose(th, want, rtol=2e-6, atol=0), t
+
+
+def test_adam_decoupled_weight_decay_alone():
+    """g = 0 everywhere: m = v = 0, the Adam term is 0/(0+eps) = 0, and the
+    decoupled decay gives theta_t = theta_0 (1 - lr wd)^t."""
+    theta0 = np.array([0.02, -1.5, 3.0, 1e-30], np.float32)
+    h = O.Hyper(lr=1e-2, weight_decay=0.1)
+    T = 40
+    hist, m, v = _adam_run([np.zeros(4, np.float32)] * T, theta0, h)
+    assert not m.any() and not v.any()
+    k = 1.0 - float(np.float32(1e-2)) * float(np.float32(0.1))
+    for t, th in enumerate(hist, 1):
+        assert np.allclose(th, theta0.astype(np.float64) * k**t, rtol=2e-7 * t, atol=0)
+
+
+def test_adam_beta1_zero_alternating_sign():
+    """beta1 = 0 and g_t = +c, -c, +c, ...: m' = g_t and v_hat = c^2 at every
+    t, so theta moves by -lr c/(c+eps) then back by +lr c/(c+eps)."""
+    c = np.float32(2e-3)
+    theta0 = np.array([0.1], np.float32)
+    h = O.Hyper(lr=1e-3, beta1=0.0, beta2=0.99, eps=1e-8)
+    seq = [np.array([c if t % 2 else -c], np.float32) for t in range(1, 21)]
+    hist, _, _ = _adam_run(seq, theta0, h)
+    d = float(np.float32(1e-3)) * float(c) / (float(c) + float(np.float32(1e-8)))
+    for t, th in enumerate(hist, 1):
+        want = 0.1 - d if t % 2 else 0.1
+        assert abs(float(th[0]) - want) <= 4 * np.spacing(np.float32(0.1))
+
+
+# ---------------------------------------------------------- a2 norm + clip
+
+def test_sumsq_all_equal_closed_form():
+    """All ranks send c and all elements equal: gbar = c, sum of squares
+    n c^2 exactly, norm |c| sqrt(n) = |c| 2^k for n = 4^k."""
+    for c, k in [(0.75, 10), (-3.0, 6), (2.0**-20, 8)]:
+        n = 4**k
+        rows = [np.full(n, _bf16_bits([c])[0], np.uint16) for _ in range(4)]
+        g, s = O.gbar_sumsq(rows, threads=3)
+        assert s == n * c * c
+        assert np.sqrt(s) == abs(c) * 2**k
+        assert O.clip_coef(s, 1.0) == min(1.0, 1.0 / (abs(c) * 2**k + 1e-6))
+
+
+def test_clip_inactive_is_unclipped_and_scaling_halves_coef():
+    w = S.by_name("tiny-zero1")
+    n = 50_000
+    rows = S.host_contrib(w, 1, 0, n)
+    g, s = O.gbar_sumsq(list(rows))
+    norm = np.sqrt(s)
+    base = dict(lr=1e-3, t=1)
+    outs = []
+    for max_norm in (0.0, norm * 1.5, norm * 100):
+        master, m, v = S.host_state(w, 0, n)
+        outs.append((O.step(list(rows), master, m, v, O.Hyper(max_norm=max_norm, **base)), master))
+    for o, mst in outs[1:]:
+        assert np.array_equal(mst, outs[0][1]) and np.array_equal(o.p, outs[0][0].p)
+    # doubling every contribution (exact in bf16) quadruples the sum of squares
+    rows2 = (rows.astype(np.uint32) + (1 << 7)).astype(np.uint16)  # exponent + 1
+    rows2[rows == 0] = 0
+    _, s2 = O.gbar_sumsq(list(rows2))
+    assert s2 == 4 * s
+    c1, c2 = O.clip_coef(s, norm / 4), O.clip_coef(s2, norm / 4)
+    assert c1 == pytest.approx(0.25, rel=1e-4) and c2 == pytest.approx(c1 / 2, rel=1e-4)
+
+
+def test_sumsq_thread_and_chunk_invariance():
+    w = S.by_name("tiny-zero1")
+    rows = S.host_contrib(w, 2, 0, w.shard_len)
+    r = [O.gbar_sumsq(list(rows), threads=t) for t in (1, 2, 5)]
+    assert r[0][1] == r[1][1] == r[2][1]
+    assert np.array_equal(r[0][0], r[2][0])
+
+
+# -------------------------------------------------------------- a5 quantize
+
+def test_quant_hand_tables():
+    g = json.load(open(os.path.join(GOLDEN, "quant_ties.json")))
+    for c in g["cases"]:
+        codes, scales = O.quant_int8(_bf16_bits(c["p"]), c["block"])
+        assert codes.tolist() == c["codes"], c["why"]
+        assert scales.tolist() == c["scales"], c["why"]
+
+
+def test_quant_structure_on_draws():
+    """On seeded bf16 shards: the absmax element of each block codes to
+    +-127, every code reconstructs its value within half a step, the code
+    of -p is -code(p), and a block's codes depend on that block only."""
+    p = S.host_bf16(256 * 40 + 32, 11, S.AUX, 0, 0, 0, 0.02)
+    codes, scales = O.quant_int8(p, 256)
+    assert scales.size == 41
+    x = _bf16_to_float(p).astype(np.float64)
+    for b in range(41):
+        blk = slice(b * 256, min((b + 1) * 256, p.size))
+        a = np.abs(x[blk]).max()
+        assert abs(scales[b] - a / 127) <= np.spacing(np.float32(a / 127))
+        assert np.abs(codes[blk]).max() == 127
+        err = np.abs(codes[blk] * float(scales[b]) - x[blk])
+        assert np.all(err <= (0.5 + 1e-5) * float(scales[b]))
+    neg = (p ^ np.uint16(0x8000)).astype(np.uint16)
+    c2, s2 = O.quant_int8(neg, 256)
+    assert np.array_equal(c2, -codes) and np.array_equal(s2, scales)
+    # the tail block of 32 alone gives the same codes as inside the shard
+    ct, st = O.quant_int8(p[-32:], 256)
+    assert np.array_equal(ct, codes[-32:]) and st[0] == scales[-1]
+
+
+# ------------------------------------------------------------- whole step
+
+def _whole_step(w, n, steps, threads=1, quant_block=0, max_norm=0.0):
+    master, m, v = S.host_state(w, 0, n)
+    out = None
+    for s in range(1, steps + 1):
+        rows = S.host_contrib(w, s, 0, n)
+        h = O.Hyper(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps,
+                    weight_decay=w.weight_decay, t=w.t_of(s), max_norm=max_norm,
+                    quant_block=quant_block)
+        out = O.step(list(rows), master, m, v, h, threads=threads)
+    return master, m, v, out
+
+
+def test_shard_concatenation_equals_unpartitioned():
+    """Elementwise independence ("ZeRO-1": a parameter's optimizer state
+    depends only on its own gradient): updating N_d shards separately and
+    concatenating equals updating the whole flat buffer, bit for bit."""
+    w = S.by_name("tiny-zero1")
+    n = 3 * 65536 + 1000
+    whole = _whole_step(w, n, 3, quant_block=256)
+    nd = 4
+    per = -(-n // nd)
+    per = -(-per // 256) * 256  # shard boundaries on block boundaries
+    parts = []
+    for r in range(nd):
+        lo, hi = r * per, min(n, (r + 1) * per)
+        master, m, v = S.host_state(w, lo, hi - lo)
+        for s in range(1, 4):
+            rows = S.host_contrib(w, s, lo, hi - lo)
+            out = O.step(list(rows), master, m, v,
+                         O.Hyper(lr=w.lr, t=s, quant_block=256))
+        parts.append((master, m, v, out))
+    assert np.array_equal(np.concatenate([p[0] for p in parts]), whole[0])
+    assert np.array_equal(np.concatenate([p[1] for p in parts]), whole[1])
+    assert np.array_equal(np.concatenate([p[2] for p in parts]), whole[2])
+    assert np.array_equal(np.concatenate([p[3].p for p in parts]), whole[3].p)
+    assert np.array_equal(np.concatenate([p[3].codes for p in parts]), whole[3].codes)
+    assert np.array_equal(np.concatenate([p[3].scales for p in parts]), whole[3].scales)
+
+
+def test_step_thread_invariance():
+    w = S.by_name("13B-nd16-clip-int8")
+    n = (1 << 20) * 2 + 777
+    a = _whole_step(w, n, 2, threads=1, quant_block=256, max_norm=1.0)
+    b = _whole_step(w, n, 2, threads=4, quant_block=256, max_norm=1.0)
+    for x, y in zip(a[:3], b[:3]):
+        assert np.array_equal(x, y)
+    assert a[3].sumsq == b[3].sumsq
+    assert np.array_equal(a[3].codes, b[3].codes)
+
+
+def test_step_empty_shard_and_bad_args():
+    h = O.Hyper()
+    e = np.zeros(0, np.float32)
+    out = O.step([np.zeros(0, np.uint16)] * 3, e, e.copy(), e.copy(), h)
+    assert out.p.size == 0 and out.sumsq == 0.0
+    with pytest.raises(ValueError):
+        O.step([np.zeros(4, np.uint16)], np.zeros(4, np.float32), np.zeros(4, np.float32),
+               np.zeros(4, np.float32), O.Hyper(t=0))
