@@ -1,0 +1,225 @@
+#!/usr/bin/env python3
+"""Benchmark of one rank's ZeRO-1/2 shard optimizer step on one MI355X.
+
+A step is one pass of the whole hot path over one batch of synthetic input
+resident in HBM: the global-norm pass (rank-order reduce + average of the
+N_d bf16 contributions, sum of squares, fp32 spill of the averaged
+gradient) and the fused update (clip, AdamW on fp32 master/m/v, bf16 cast,
+int8 block quantization).  Default workload: the 13B-parameter model at
+N_d = 16 with clipping and int8 output, the one workload that runs every
+step of the path; ``--config`` selects another.
+
+Prints one JSON line: params updated per second (``value``), the roofline
+of the dominant kernel (algorithmic bytes per launch / its mean duration
+from HIP events on the launch stream, against the 8 TB/s HBM peak) and the
+CPU oracle's rate on a bounded sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "params updated/sec and achieved HBM GB/s (% of peak) per ZeRO shard step"
+DEFAULT_WORKLOAD = "13B-nd16-clip-int8"
+
+
+def _eprint(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_bytes(w, spill: bool = True) -> dict[str, float]:
+    """Algorithmic HBM bytes per shard element of each launch of a step."""
+    q = (1.0 + 4.0 / w.quant_block) if w.quant_block else 0.0
+    if w.max_norm > 0:
+        norm = 2.0 * w.n_d + (4.0 if spill else 0.0)        # rows in, fp32 spill out
+        upd = (4.0 if spill else 2.0 * w.n_d) + 24.0 + 2.0 + q  # spill in, state, bf16
+        return {"gnorm": norm, "step": upd}
+    return {"step": 2.0 * w.n_d + 24.0 + 2.0 + q}
+
+
+def cpu_baseline(w, target_s: float = 12.0) -> dict:
+    """The oracle, as it stands, on the first S elements of this workload's
+    shard for one step (clipping uses the norm of the sample), timed on the
+    host cores; S is sized for ~target_s seconds of CPU work."""
+    import numpy as np
+
+    import oracle as O
+    import seeded_inputs as S
+
+    try:
+        threads = max(1, min(16, len(os.sched_getaffinity(0))))
+    except AttributeError:
+        threads = max(1, min(16, os.cpu_count() or 1))
+
+    def run(n):
+        rows = list(S.host_contrib(w, 1, 0, n))
+        master, m, v = S.host_state(w, 0, n)
+        h = O.Hyper(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps,
+                    weight_decay=w.weight_decay, t=w.t_of(1), max_norm=w.max_norm,
+                    quant_block=w.quant_block)
+        t0 = time.perf_counter()
+        O.step(rows, master, m, v, h, threads=threads)
+        return time.perf_counter() - t0
+
+    n0 = min(1 << 20, w.shard_len)
+    t0 = run(n0)
+    n = int(min(w.shard_len, max(n0, n0 * target_s / max(t0, 1e-6)), 1 << 27))
+    n = max(1, n // 256 * 256) if n > 256 else n
+    dt = run(n)
+    return {"value": n / dt, "unit": "params/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {n} of {w.shard_len} shard elements of {w.name}, one step "
+                      f"(norm over the sample), {threads} threads, {dt:.2f} s",
+            "seconds": round(dt, 3)}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default=DEFAULT_WORKLOAD,
+                    help="workload name or index (default: %(default)s)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-spill", action="store_true",
+                    help="clipped steps re-read the contributions instead of the fp32 spill")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run torch copies of MIB MiB (for HBM counter scaling)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one rank's shard step on one GPU; this build has no "
+              "multi-GPU path (run with --gpus 1)", file=sys.stderr)
+        return 2
+
+    import torch
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+
+    if args.copy_calibration:
+        nbytes = args.copy_calibration << 20
+        a = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+        b = torch.empty_like(a)
+        for _ in range(max(1, args.steps)):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": nbytes, "copy_bytes_written": nbytes,
+                          "launches": max(1, args.steps)}))
+        return 0
+
+    import seeded_inputs as S
+    from tests._gpu import GpuShard
+
+    w = S.by_name(args.config)
+    spill = not args.no_spill
+    n = w.shard_len
+    _eprint(f"[bench] workload {w.name}: shard {n} of phi {w.phi}, n_d {w.n_d}, "
+            f"clip {w.max_norm}, int8 block {w.quant_block}, spill {spill and w.max_norm > 0}")
+    g = GpuShard(w, spill=spill)
+    g.init_state()
+    g.fill_grads(1)  # resident contributions, reused by every timed step
+    torch.cuda.synchronize()
+    _eprint("[bench] inputs resident; warmup")
+
+    stream = torch.cuda.current_stream()
+    kb = kernel_bytes(w, spill)
+
+    def one_step(s, ev=None):
+        lr = w.lr
+        if g.clip:
+            if ev is not None:
+                ev[0].record(stream)
+            g.shard.gnorm(g.rows, g.sumsq)
+            if ev is not None:
+                ev[1].record(stream)
+            g.shard.step(None if g.gbar_ws is not None else g.rows, lr, w.t_of(s), g.sumsq)
+            if ev is not None:
+                ev[2].record(stream)
+        else:
+            if ev is not None:
+                ev[1].record(stream)
+            g.shard.step(g.rows, lr, w.t_of(s))
+            if ev is not None:
+                ev[2].record(stream)
+
+    for s in range(1, args.warmup + 1):
+        one_step(s)
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        one_step(args.warmup + 1 + i, evs[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    _eprint(f"[bench] timed {args.steps} steps in {elapsed * 1e3:.2f} ms")
+
+    dur = {"step": [e[1].elapsed_time(e[2]) for e in evs]}
+    if g.clip:
+        dur["gnorm"] = [e[0].elapsed_time(e[1]) for e in evs]
+    mean_ms = {k: sum(v) / len(v) for k, v in dur.items()}
+    dominant = max(mean_ms, key=mean_ms.get)
+    per_kernel = {}
+    for k, ms in mean_ms.items():
+        gbs = kb[k] * n / (ms * 1e-3) / 1e9
+        per_kernel[k] = {"mean_ms": round(ms, 4), "bytes_per_param": kb[k],
+                         "GBps": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4)}
+        _eprint(f"[bench] {k}: {ms:.4f} ms, {kb[k]:.3f} B/param, {gbs:.1f} GB/s "
+                f"({100 * gbs / HBM_PEAK_GBS:.1f}% of 8 TB/s)")
+    ms_step = elapsed * 1e3 / args.steps
+    step_bpp = sum(kb.values())
+    step_gbs = step_bpp * n / (ms_step * 1e-3) / 1e9
+    value = n / (ms_step * 1e-3)
+    ach = per_kernel[dominant]["GBps"]
+    g.free()
+    del g
+    torch.cuda.empty_cache()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        _eprint("[bench] CPU oracle baseline on a bounded sample")
+        cpu = cpu_baseline(w)
+        _eprint(f"[bench] oracle: {cpu['value']:.3e} params/s ({cpu['sample']})")
+
+    kernel_names = {"gnorm": "gnorm_partial_kernel (+ gnorm_final_kernel)",
+                    "step": f"step_kernel<{w.quant_block // 8 if w.quant_block else 0}>"}
+    line = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "params/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f64",
+        "data": "synthetic",
+        "config": {"workload": w.name, "phi": w.phi, "n_d": w.n_d, "r": w.r, "shard_len": n,
+                   "max_norm": w.max_norm, "weight_decay": w.weight_decay,
+                   "quant_block": w.quant_block, "grad_spill": bool(spill and w.max_norm > 0),
+                   "parallelism": f"one rank of dp{w.n_d}"},
+        "hbm": {"bytes_per_param": step_bpp, "GBps": round(step_gbs, 1),
+                "frac": round(step_gbs / HBM_PEAK_GBS, 4), "kernels": per_kernel},
+        "roofline": {"bound": "hbm", "kernel": kernel_names[dominant], "achieved": ach,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
+                     "traffic": None},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

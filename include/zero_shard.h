@@ -1,0 +1,156 @@
+/*
+ * zero_shard.h -- C ABI of the MI355X (gfx950) ZeRO-1/2 shard optimizer step.
+ *
+ * One data-parallel rank owns partition r of the flat parameter vector
+ * theta = [theta_1 .. theta_N] and keeps the fp32 optimizer state for that
+ * partition only ("Data parallelism and ZeRO optimization", sections
+ * "ZeRO-1: Optimizer State Partitioning" and "ZeRO-2: Gradient
+ * Partitioning"; "ZeRO (딥 러닝)", stage table of "ZeRO-DP의 세 단계").
+ * Between the reduce-scatter of the gradients and the all-gather of the
+ * updated weights ("ZeRO (딥 러닝)", "왜 통신량이 늘지 않는가") the rank:
+ *
+ *   a1  sums the N_d incoming bf16 gradient contributions for its slice in
+ *       rank order and averages them ("大模型并行技术", "优化状态与梯度分割",
+ *       step 2; "How Standard Data Parallelism Works": the average);
+ *   a2  optionally clips by the global L2 norm of the averaged gradient
+ *       ("ZeRO (딥 러닝)", "DeepSpeed에서 쓰기": gradient_clipping);
+ *   a3  runs mixed-precision AdamW on its fp32 master weights, momentum and
+ *       variance ("Memory Consumption Analysis"; "精度混合训练");
+ *   a4  writes the bf16 copy of the updated master weights, the buffer the
+ *       all-gather sends;
+ *   a5  optionally block-quantizes that copy to int8 codes plus one fp32
+ *       scale per block (ZeRO++ qwZ, "ZeRO (딥 러닝)", follow-ups table
+ *       "후속 기법").
+ *
+ * Arithmetic (what every call computes, element i of the shard):
+ *   s_i    = sum_{k=0}^{n_d-1} bf16(contrib[k][i])   binary64, k ascending
+ *   gbar_i = binary32(s_i / n_d)                      one rounding
+ *   g_i    = coef * gbar_i                            binary64; coef = 1
+ *            unless clipping: coef = min(1, max_norm / (sqrt(S) + 1e-6)),
+ *            S = global sum of gbar^2 handed to zero_shard_step
+ *   m'     = b1 m + (1-b1) g        v' = b2 v + (1-b2) (g g)
+ *   theta' = theta - (lr wd) theta - lr (m'/bc1) / (sqrt(v'/bc2) + eps)
+ *            bc = 1 - beta^t with bias correction, else 1; all binary64
+ *            from the binary32 state, each result rounded once to binary32
+ *   p_i    = bf16(theta'_i), round to nearest even
+ *   int8:  block b = elements [b*B, b*B+B) of the shard (last one partial);
+ *          a = max |p|, scale = binary32(a / 127), code = round-half-even(
+ *          binary32(p / scale)) clamped to +-127; scale 0 => codes 0;
+ *          a non-finite quotient gives code 0.
+ * Non-finite inputs propagate per IEEE; no step is skipped.
+ *
+ * Memory: every pointer in zs_desc and every contribution pointer is a
+ * device pointer (HBM of the current device), allocated and owned by the
+ * caller, and must stay valid until the work queued on the stream is done.
+ * Layouts are flat, contiguous, element i at offset i.  fp32 and bf16
+ * arrays and every contribution row must be 16-byte aligned; q_codes 8-byte
+ * aligned.  The library owns only the handle and a small device scratch
+ * (fp64 block partials of the norm, <= 16 KiB), allocated at init.
+ *
+ * Errors: every call returns ZS_OK (0) or a negative zs_status.  Arguments
+ * are validated before anything is queued: on an error nothing is launched
+ * and no output is touched.  Launch failures are reported as ZS_EHIP;
+ * faults inside a kernel surface at the caller's next synchronisation.
+ * Calls are asynchronous on the handle's stream; a handle is used by one
+ * host thread at a time.
+ */
+#ifndef ZERO_SHARD_H
+#define ZERO_SHARD_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct zs_handle zs_handle; /* opaque */
+typedef uint16_t zs_bf16;           /* bf16 bit pattern */
+
+typedef enum zs_status {
+  ZS_OK = 0,
+  ZS_EINVAL = -1,  /* bad size, index, hyper-parameter or missing pointer */
+  ZS_EALIGN = -2,  /* a pointer is not aligned as required                */
+  ZS_ENOMEM = -3,  /* the library's own scratch could not be allocated     */
+  ZS_EHIP = -4,    /* a HIP runtime call or kernel launch failed           */
+  ZS_EDEVICE = -5, /* the current device is not gfx950                     */
+  ZS_ESTATE = -6   /* call out of order (step reading a gradient spill
+                      that no norm pass has written) or a dead handle      */
+} zs_status;
+
+#define ZS_MAX_ND 64 /* most contributions one call can average */
+
+typedef struct zs_desc {
+  /* partition geometry */
+  int64_t phi;       /* parameters in the whole flat buffer, >= 0           */
+  int32_t n_d;       /* data-parallel degree, 1..ZS_MAX_ND                  */
+  int32_t r;         /* partition index, 0 <= r < n_d                       */
+  int64_t shard_len; /* elements of partition r: min(ceil(phi/n_d),
+                        phi - r*ceil(phi/n_d)) clamped at 0; or phi with
+                        r == 0 for the unpartitioned (stage 0) update        */
+  /* optimizer: binary32 values, used widened to binary64 */
+  float beta1, beta2; /* in [0, 1)                                          */
+  float eps;          /* > 0                                                */
+  float weight_decay; /* >= 0, decoupled; 0 = plain Adam                    */
+  int32_t bias_correction; /* 1: divide by 1 - beta^t; 0: do not          */
+  float max_norm;     /* > 0: clip by the global norm; <= 0: no clipping   */
+  int32_t quant_block; /* 0: no int8; else 32, 64, 128, 256 or 512: the
+                          step also writes codes and scales (fused)        */
+  /* state and outputs (device pointers, caller-owned) */
+  float *master, *m, *v; /* fp32[shard_len], updated in place              */
+  zs_bf16 *param_out;    /* bf16[shard_len]                                */
+  int8_t *q_codes;       /* int8[shard_len]; needed iff quant_block > 0 or
+                            zero_shard_quant is called                     */
+  float *q_scales;       /* fp32[ceil(shard_len / block)], same condition  */
+  float *gbar_ws;        /* optional fp32[shard_len] workspace; with
+                            clipping, zero_shard_gnorm stores the averaged
+                            gradient there and zero_shard_step reads it
+                            instead of re-reading the contributions        */
+  void *stream;          /* hipStream_t for every call; NULL = null stream */
+} zs_desc;
+
+/* Validate d, check that the current device is gfx950, allocate the norm
+ * scratch, and return a handle in *out.  The descriptor is copied.
+ * Errors: ZS_EINVAL, ZS_EALIGN, ZS_EDEVICE, ZS_ENOMEM, ZS_EHIP. */
+int zero_shard_init(const zs_desc *d, zs_handle **out);
+
+/* a2, first sweep: this shard's sum of squares of the averaged gradient,
+ * S_local = sum_i gbar_i^2 (binary64), reduced over a fixed grid in a fixed
+ * order with no atomics (same inputs => same bits).  contrib is a HOST
+ * array of n_d device pointers, contrib[k] = rank k's bf16 gradient for
+ * this shard (shard-local index).  Writes S_local to *sumsq_dev (device,
+ * one double).  With gbar_ws set, also stores gbar there for the next step.
+ * Summing S_local over the shards (one scalar all-reduce across ranks) gives
+ * the S that zero_shard_step takes.  Errors: ZS_EINVAL, ZS_EALIGN, ZS_EHIP,
+ * ZS_ESTATE. */
+int zero_shard_gnorm(zs_handle *h, const zs_bf16 *const *contrib, double *sumsq_dev);
+
+/* a1 + a3 + a4 (+ a5 when quant_block > 0): one optimizer step at 1-based
+ * step counter t with learning rate lr >= 0.  contrib as for gnorm; it may
+ * be NULL when clipping with gbar_ws (the spill written by the preceding
+ * zero_shard_gnorm is read instead).  global_sumsq_dev (device, one double)
+ * is S and is required iff max_norm > 0; it is read on the device, so no
+ * host synchronisation is needed between gnorm and step.
+ * Errors: ZS_EINVAL, ZS_EALIGN, ZS_ESTATE, ZS_EHIP. */
+int zero_shard_step(zs_handle *h, const zs_bf16 *const *contrib, float lr, int64_t t,
+                    const double *global_sumsq_dev);
+
+/* a5 as a separate pass: quantize param_out into q_codes / q_scales with
+ * the given block (32, 64, 128, 256 or 512); q_scales must hold
+ * ceil(shard_len / block) floats.  Errors: ZS_EINVAL, ZS_EHIP. */
+int zero_shard_quant(zs_handle *h, int32_t block);
+
+/* Wait for the handle's stream, release its scratch and the handle.
+ * Passing NULL is a no-op returning ZS_OK. */
+int zero_shard_free(zs_handle *h);
+
+/* Static description of a status code (never NULL). */
+const char *zero_shard_strerror(int code);
+
+/* Length of partition r of phi parameters over n_d ranks (the geometry
+ * zero_shard_init checks), or -1 for invalid arguments. */
+int64_t zero_shard_len(int64_t phi, int32_t n_d, int32_t r);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* ZERO_SHARD_H */

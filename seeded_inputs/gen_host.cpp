@@ -60,13 +60,27 @@ void zsg_host_fill_bf16(uint16_t *out, int64_t n, uint64_t seed, uint32_t tid,
 }
 
 /* Rows k = 0..n_d-1 of one step's gradient contributions, row k at
- * out + k*row_stride, elements [i0, i0+n) of each rank's shard slice. */
+ * out + k*row_stride, elements [i0, i0+n) of each rank's shard slice.
+ * With many rows the threads take whole rows; with few, each row is split. */
 void zsg_host_fill_contrib(uint16_t *out, int32_t n_d, int64_t row_stride,
                            int64_t n, uint64_t seed, uint32_t step, int64_t i0,
                            float sigma, int outliers, int threads) {
+  if (threads < 1) threads = 1;
+  if (n_d >= threads || n < (int64_t(1) << 17)) {
+    const int t = threads < n_d ? threads : n_d;
+    std::vector<std::thread> pool;
+    for (int w = 0; w < t; ++w)
+      pool.emplace_back([=] {
+        for (int32_t k = w; k < n_d; k += t)
+          zsg_host_fill_bf16(out + k * row_stride, n, seed, ZSG_GRAD, step, uint32_t(k), i0,
+                             sigma, outliers, 1);
+      });
+    for (auto &th : pool) th.join();
+    return;
+  }
   for (int32_t k = 0; k < n_d; ++k)
-    zsg_host_fill_bf16(out + k * row_stride, n, seed, ZSG_GRAD, step, uint32_t(k),
-                       i0, sigma, outliers, threads);
+    zsg_host_fill_bf16(out + k * row_stride, n, seed, ZSG_GRAD, step, uint32_t(k), i0, sigma,
+                       outliers, threads);
 }
 
 }  // extern "C"

@@ -1,0 +1,195 @@
+"""Python binding of the MI355X ZeRO-1/2 shard optimizer step.
+
+Argument marshalling only: every step of the path runs in the HIP kernels of
+``libzeroshard.so`` behind the C ABI of ``include/zero_shard.h``.  The
+functions below carry the C names; ``ZeroShard`` is a small owner object
+over one handle.  PyTorch is used for device memory and streams only.
+
+There is no fallback: importing this package without the built library
+raises, and every call that returns a negative status raises ``ZeroShardError``.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libzeroshard.so")
+
+ZS_OK, ZS_EINVAL, ZS_EALIGN, ZS_ENOMEM, ZS_EHIP, ZS_EDEVICE, ZS_ESTATE = 0, -1, -2, -3, -4, -5, -6
+ZS_MAX_ND = 64
+QUANT_BLOCKS = (32, 64, 128, 256, 512)
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() (hipcc, gfx950)")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+
+class zs_desc(ctypes.Structure):  # noqa: N801  (the C name)
+    _fields_ = [
+        ("phi", ctypes.c_int64),
+        ("n_d", ctypes.c_int32),
+        ("r", ctypes.c_int32),
+        ("shard_len", ctypes.c_int64),
+        ("beta1", ctypes.c_float),
+        ("beta2", ctypes.c_float),
+        ("eps", ctypes.c_float),
+        ("weight_decay", ctypes.c_float),
+        ("bias_correction", ctypes.c_int32),
+        ("max_norm", ctypes.c_float),
+        ("quant_block", ctypes.c_int32),
+        ("master", ctypes.c_void_p),
+        ("m", ctypes.c_void_p),
+        ("v", ctypes.c_void_p),
+        ("param_out", ctypes.c_void_p),
+        ("q_codes", ctypes.c_void_p),
+        ("q_scales", ctypes.c_void_p),
+        ("gbar_ws", ctypes.c_void_p),
+        ("stream", ctypes.c_void_p),
+    ]
+
+
+_handle_p = ctypes.c_void_p
+_lib.zero_shard_init.restype = ctypes.c_int
+_lib.zero_shard_init.argtypes = [ctypes.POINTER(zs_desc), ctypes.POINTER(_handle_p)]
+_lib.zero_shard_gnorm.restype = ctypes.c_int
+_lib.zero_shard_gnorm.argtypes = [_handle_p, ctypes.c_void_p, ctypes.c_void_p]
+_lib.zero_shard_step.restype = ctypes.c_int
+_lib.zero_shard_step.argtypes = [_handle_p, ctypes.c_void_p, ctypes.c_float, ctypes.c_int64,
+                                 ctypes.c_void_p]
+_lib.zero_shard_quant.restype = ctypes.c_int
+_lib.zero_shard_quant.argtypes = [_handle_p, ctypes.c_int32]
+_lib.zero_shard_free.restype = ctypes.c_int
+_lib.zero_shard_free.argtypes = [_handle_p]
+_lib.zero_shard_strerror.restype = ctypes.c_char_p
+_lib.zero_shard_strerror.argtypes = [ctypes.c_int]
+_lib.zero_shard_len.restype = ctypes.c_int64
+_lib.zero_shard_len.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32]
+
+EXPORTS = ("zero_shard_init", "zero_shard_gnorm", "zero_shard_step", "zero_shard_quant",
+           "zero_shard_free", "zero_shard_strerror", "zero_shard_len")
+
+
+class ZeroShardError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        self.code = code
+        super().__init__(f"{what}: {zero_shard_strerror(code)} ({code})")
+
+
+def _check(rc: int, what: str) -> None:
+    if rc != ZS_OK:
+        raise ZeroShardError(rc, what)
+
+
+def _ptr(t) -> int | None:
+    if t is None:
+        return None
+    return int(t.data_ptr())
+
+
+def contrib_table(contrib) -> ctypes.Array | None:
+    """Host array of device pointers: a list of 1-D 16-bit tensors, or the
+    rows of a 2-D 16-bit tensor (row k = rank k's contribution)."""
+    if contrib is None:
+        return None
+    if hasattr(contrib, "dim") and contrib.dim() == 2:
+        rows = [contrib[k] for k in range(contrib.shape[0])]
+    else:
+        rows = list(contrib)
+    tab = (ctypes.c_void_p * max(1, len(rows)))(*[_ptr(r) for r in rows])
+    tab._keep = rows
+    return tab
+
+
+# ------------------------------------------------------------ C-named calls
+
+def zero_shard_strerror(code: int) -> str:
+    return _lib.zero_shard_strerror(int(code)).decode()
+
+
+def zero_shard_len(phi: int, n_d: int, r: int) -> int:
+    return int(_lib.zero_shard_len(int(phi), int(n_d), int(r)))
+
+
+def zero_shard_init(desc: zs_desc) -> tuple[int, ctypes.c_void_p]:
+    h = _handle_p()
+    rc = _lib.zero_shard_init(ctypes.byref(desc), ctypes.byref(h))
+    return rc, h
+
+
+def zero_shard_gnorm(h, contrib, sumsq_dev) -> int:
+    return _lib.zero_shard_gnorm(h, contrib_table(contrib), _ptr(sumsq_dev))
+
+
+def zero_shard_step(h, contrib, lr: float, t: int, global_sumsq_dev=None) -> int:
+    return _lib.zero_shard_step(h, contrib_table(contrib), float(lr), int(t),
+                                _ptr(global_sumsq_dev))
+
+
+def zero_shard_quant(h, block: int) -> int:
+    return _lib.zero_shard_quant(h, int(block))
+
+
+def zero_shard_free(h) -> int:
+    return _lib.zero_shard_free(h)
+
+
+# ------------------------------------------------------------- owner object
+
+class ZeroShard:
+    """One rank's shard step over caller-owned torch tensors.
+
+    master, m, v: float32[shard_len]; param_out: 16-bit [shard_len] (bf16
+    patterns); q_codes int8[shard_len] and q_scales float32[ceil(n/block)]
+    when quantizing; gbar_ws float32[shard_len] optional (clipping spill).
+    All on the current device.  ``stream`` is a torch stream (default: the
+    current stream at construction)."""
+
+    def __init__(self, *, phi: int, n_d: int, r: int, shard_len: int, master, m, v, param_out,
+                 beta1: float = 0.9, beta2: float = 0.999, eps: float = 1e-8,
+                 weight_decay: float = 0.0, bias_correction: bool = True,
+                 max_norm: float = 0.0, quant_block: int = 0, q_codes=None, q_scales=None,
+                 gbar_ws=None, stream=None):
+        if stream is None:
+            import torch
+
+            stream = torch.cuda.current_stream()
+        self._keep = (master, m, v, param_out, q_codes, q_scales, gbar_ws, stream)
+        self.desc = zs_desc(
+            phi=int(phi), n_d=int(n_d), r=int(r), shard_len=int(shard_len),
+            beta1=beta1, beta2=beta2, eps=eps, weight_decay=weight_decay,
+            bias_correction=int(bool(bias_correction)), max_norm=max_norm,
+            quant_block=int(quant_block), master=_ptr(master), m=_ptr(m), v=_ptr(v),
+            param_out=_ptr(param_out), q_codes=_ptr(q_codes), q_scales=_ptr(q_scales),
+            gbar_ws=_ptr(gbar_ws), stream=int(stream.cuda_stream))
+        rc, self.h = zero_shard_init(self.desc)
+        _check(rc, "zero_shard_init")
+
+    def gnorm(self, contrib, sumsq_dev) -> None:
+        _check(zero_shard_gnorm(self.h, contrib, sumsq_dev), "zero_shard_gnorm")
+
+    def step(self, contrib, lr: float, t: int, global_sumsq_dev=None) -> None:
+        _check(zero_shard_step(self.h, contrib, lr, t, global_sumsq_dev), "zero_shard_step")
+
+    def quant(self, block: int) -> None:
+        _check(zero_shard_quant(self.h, block), "zero_shard_quant")
+
+    def free(self) -> None:
+        if self.h is not None and self.h.value:
+            _check(zero_shard_free(self.h), "zero_shard_free")
+        self.h = None
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.free()
+
+    def __del__(self):
+        try:
+            if getattr(self, "h", None) is not None and self.h.value:
+                zero_shard_free(self.h)
+        except Exception:
+            pass

@@ -1,0 +1,692 @@
+// zero_shard.hip -- MI355X (gfx950) kernels and C ABI of the ZeRO-1/2 shard
+// optimizer step (declarations and the contract: include/zero_shard.h).
+//
+// The step is HBM-bound elementwise work, so there is no MFMA here.  Design
+// for CDNA4:
+//  * one lane owns 8 consecutive shard elements: each contribution row is one
+//    128-bit load, each fp32 state array two, the bf16 output one 128-bit
+//    store; a wave64 touches 1 KiB of every row per access, fully coalesced;
+//  * the rank-order sum of the bf16 contributions runs in binary64 registers
+//    (full-rate fp64 on CDNA), exact for these addends; the average is
+//    rounded once to binary32, the precision the reduce-scatter delivers;
+//  * rows are loaded in groups of kRowGroup so that many 16-byte loads per
+//    lane are in flight while the sum keeps its fixed k order;
+//  * the AdamW update runs in binary64 from the binary32 state with every
+//    result rounded once on store (IEEE division and square root), the bf16
+//    cast uses the gfx950 v_cvt_pk_bf16_f32 conversion (nearest even);
+//  * the int8 block quantizer is fused into the same pass: a block of B
+//    elements is B/8 adjacent lanes of one wave, its absmax a lane-shuffle
+//    reduction, so quantization adds only the code and scale writes;
+//  * the global norm is a fixed-grid, fixed-order two-kernel reduction
+//    (fp64 block partials, then one block) with no atomics, so identical
+//    inputs give identical bits.
+// All arithmetic is exactly as written (built with -ffp-contract=off, no
+// fast-math, denormals preserved).
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <new>
+#include <unordered_set>
+
+#include "zero_shard.h"
+
+namespace {
+
+using u32x4 = unsigned int __attribute__((ext_vector_type(4)));
+using u32x2 = unsigned int __attribute__((ext_vector_type(2)));
+using f32x4 = float __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 256;    // 4 waves per workgroup
+constexpr int kVec = 8;          // shard elements per lane
+#ifndef ZS_ROW_GROUP
+#define ZS_ROW_GROUP 8
+#endif
+constexpr int kRowGroup = ZS_ROW_GROUP;  // contribution rows loaded together
+constexpr int kNormBlocks = 2048;        // fixed grid of the norm pass
+#ifndef ZS_BLOCKS_PER_CU
+#define ZS_BLOCKS_PER_CU 8
+#endif
+
+struct Rows {
+  const u32x4 *p[ZS_MAX_ND];  // row k = rank k's contribution for this shard
+};
+
+struct AdamConst {
+  double b1, omb1;  // beta1, 1 - beta1
+  double b2, omb2;  // beta2, 1 - beta2
+  double bc1, bc2;  // bias corrections (1 when off)
+  double lr, decay, eps;  // lr, lr * weight_decay, eps
+};
+
+struct Avg {
+  int32_t nd;
+  int32_t pow2;     // n_d is a power of two: s / n_d == s * (1 / n_d)
+  double nd_f, inv_nd;
+};
+
+struct StepArgs {
+  Rows rows;
+  Avg avg;
+  AdamConst k;
+  int64_t n;
+  const double *sumsq;  // clip by this global sum of squares iff non-null
+  double max_norm;
+  const float *gbar;    // read the averaged gradient from here iff non-null
+  float *master, *m, *v;
+  uint16_t *pout;
+  int8_t *codes;
+  float *scales;
+};
+
+struct NormArgs {
+  Rows rows;
+  Avg avg;
+  int64_t n;
+  float *gbar_out;   // store the averaged gradient iff non-null
+  double *partials;  // one per block
+};
+
+struct QuantArgs {
+  const uint16_t *p;
+  int64_t n;
+  int8_t *codes;
+  float *scales;
+};
+
+// ------------------------------------------------------------ device helpers
+
+__device__ __forceinline__ float bf16_lo(unsigned w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(unsigned w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Nearest-even bf16 of two floats, packed (lo in bits 0..15): one
+// v_cvt_pk_bf16_f32 on gfx950.
+__device__ __forceinline__ unsigned pack_bf16(float lo, float hi) {
+  const unsigned a = __builtin_bit_cast(unsigned short, static_cast<__bf16>(lo));
+  const unsigned b = __builtin_bit_cast(unsigned short, static_cast<__bf16>(hi));
+  return a | (b << 16);
+}
+
+__device__ __forceinline__ void add_row(double (&s)[kVec], const u32x4 r) {
+  s[0] += static_cast<double>(bf16_lo(r.x));
+  s[1] += static_cast<double>(bf16_hi(r.x));
+  s[2] += static_cast<double>(bf16_lo(r.y));
+  s[3] += static_cast<double>(bf16_hi(r.y));
+  s[4] += static_cast<double>(bf16_lo(r.z));
+  s[5] += static_cast<double>(bf16_hi(r.z));
+  s[6] += static_cast<double>(bf16_lo(r.w));
+  s[7] += static_cast<double>(bf16_hi(r.w));
+}
+
+__device__ __forceinline__ float average(double s, const Avg &a) {
+  return a.pow2 ? static_cast<float>(s * a.inv_nd) : static_cast<float>(s / a.nd_f);
+}
+
+// Averaged gradient of the 8 elements of lane-vector `vec`.  Full vectors
+// take 128-bit loads, rows in groups of kRowGroup; a partial vector (the
+// shard's last, nvalid < 8) loads element by element.  The additions are
+// the same in both cases: k = 0..nd-1 into a binary64 accumulator per
+// element.
+__device__ __forceinline__ void reduce_average(const Rows &rows, const Avg &avg, int64_t vec,
+                                               int nvalid, float (&g)[kVec]) {
+  double s[kVec];
+#pragma unroll
+  for (int e = 0; e < kVec; ++e) s[e] = 0.0;
+  if (nvalid == kVec) {
+    for (int k0 = 0; k0 < avg.nd; k0 += kRowGroup) {
+      u32x4 r[kRowGroup];
+#pragma unroll
+      for (int j = 0; j < kRowGroup; ++j)
+        if (k0 + j < avg.nd) r[j] = __builtin_nontemporal_load(rows.p[k0 + j] + vec);
+#pragma unroll
+      for (int j = 0; j < kRowGroup; ++j)
+        if (k0 + j < avg.nd) add_row(s, r[j]);
+    }
+  } else {
+    for (int k = 0; k < avg.nd; ++k) {
+      const uint16_t *row = reinterpret_cast<const uint16_t *>(rows.p[k]) + vec * kVec;
+#pragma unroll
+      for (int e = 0; e < kVec; ++e)
+        if (e < nvalid) s[e] += static_cast<double>(__uint_as_float(unsigned(row[e]) << 16));
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < kVec; ++e) g[e] = average(s[e], avg);
+}
+
+__device__ __forceinline__ double clip_coef(double sumsq, double max_norm) {
+  const double c = max_norm / (sqrt(sumsq) + 1e-6);
+  if (c != c) return c;  // NaN propagates
+  return c < 1.0 ? c : 1.0;
+}
+
+// AdamW on one element: binary64 from the binary32 state, one rounding per
+// stored value.  The expression order is the contract's.
+__device__ __forceinline__ void adam(double g, float &th, float &mo, float &va,
+                                     const AdamConst &k) {
+  const double m1 = k.b1 * static_cast<double>(mo) + k.omb1 * g;
+  const double v1 = k.b2 * static_cast<double>(va) + k.omb2 * (g * g);
+  const double mhat = m1 / k.bc1;
+  const double vhat = v1 / k.bc2;
+  const double t0 = static_cast<double>(th);
+  const double t1 = t0 - k.decay * t0 - k.lr * mhat / (sqrt(vhat) + k.eps);
+  mo = static_cast<float>(m1);
+  va = static_cast<float>(v1);
+  th = static_cast<float>(t1);
+}
+
+__device__ __forceinline__ float nanmax(float a, float b) {
+  if (a != a) return a;
+  return (b > a || b != b) ? b : a;
+}
+
+// int8 code of x with scale s (binary32 quotient, ties to even, +-127).
+__device__ __forceinline__ int quant_code(float x, float s) {
+  if (s == 0.0f) return 0;
+  float r = x / s;
+  if (!__builtin_isfinite(r)) return 0;
+  r = __builtin_rintf(r);
+  r = r > 127.0f ? 127.0f : (r < -127.0f ? -127.0f : r);
+  return static_cast<int>(r);
+}
+
+// Quantize the 8 bf16 values of lane-vector `vec` as part of a block of
+// QL adjacent lanes (block = 8*QL elements).  Every lane of the wave must
+// call this (the absmax is a shuffle reduction); lanes past the end pass
+// nvalid = 0.
+template <int QL>
+__device__ __forceinline__ void quant_lane(const float (&p)[kVec], int nvalid, int64_t vec,
+                                           int8_t *codes, float *scales) {
+  float a = 0.0f;
+#pragma unroll
+  for (int e = 0; e < kVec; ++e)
+    if (e < nvalid) a = nanmax(a, __builtin_fabsf(p[e]));
+#pragma unroll
+  for (int off = QL / 2; off >= 1; off >>= 1) a = nanmax(a, __shfl_xor(a, off));
+  const float s = a / 127.0f;
+  if (nvalid == kVec) {
+    unsigned lo = 0, hi = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      lo |= (unsigned(quant_code(p[e], s)) & 0xffu) << (8 * e);
+      hi |= (unsigned(quant_code(p[e + 4], s)) & 0xffu) << (8 * e);
+    }
+    u32x2 q;
+    q.x = lo;
+    q.y = hi;
+    __builtin_nontemporal_store(q, reinterpret_cast<u32x2 *>(codes) + vec);
+  } else {
+#pragma unroll
+    for (int e = 0; e < kVec; ++e)
+      if (e < nvalid) codes[vec * kVec + e] = static_cast<int8_t>(quant_code(p[e], s));
+  }
+  if (nvalid > 0 && (vec % QL) == 0) scales[vec / QL] = s;
+}
+
+// ------------------------------------------------------------------ kernels
+
+// a1 + a2 (apply) + a3 + a4 (+ a5 when QL > 0).  The loop runs over whole
+// waves so that every lane reaches the quantizer's shuffles together.
+template <int QL>
+__global__ void __launch_bounds__(kThreads) step_kernel(const StepArgs A) {
+  const int lane = threadIdx.x & 63;
+  const int64_t nvec = (A.n + kVec - 1) / kVec;
+  const int64_t stride = int64_t(gridDim.x) * kThreads;
+  const double coef = A.sumsq ? clip_coef(*A.sumsq, A.max_norm) : 1.0;
+  for (int64_t base = int64_t(blockIdx.x) * kThreads + (threadIdx.x & ~63); base < nvec;
+       base += stride) {
+    const int64_t vec = base + lane;
+    const int64_t e0 = vec * kVec;
+    const int nvalid = e0 + kVec <= A.n ? kVec : (e0 < A.n ? int(A.n - e0) : 0);
+    float th[kVec], mo[kVec], va[kVec], g[kVec], p[kVec];
+    if (nvalid == kVec) {
+      const f32x4 *t4 = reinterpret_cast<const f32x4 *>(A.master) + 2 * vec;
+      const f32x4 *m4 = reinterpret_cast<const f32x4 *>(A.m) + 2 * vec;
+      const f32x4 *v4 = reinterpret_cast<const f32x4 *>(A.v) + 2 * vec;
+      const f32x4 ta = t4[0], tb = t4[1], ma = m4[0], mb = m4[1], vx = v4[0], vy = v4[1];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        th[e] = ta[e]; th[e + 4] = tb[e];
+        mo[e] = ma[e]; mo[e + 4] = mb[e];
+        va[e] = vx[e]; va[e + 4] = vy[e];
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < kVec; ++e) {
+        const bool ok = e < nvalid;
+        th[e] = ok ? A.master[e0 + e] : 0.0f;
+        mo[e] = ok ? A.m[e0 + e] : 0.0f;
+        va[e] = ok ? A.v[e0 + e] : 0.0f;
+      }
+    }
+    if (nvalid > 0) {
+      if (A.gbar) {
+        if (nvalid == kVec) {
+          const f32x4 *g4 = reinterpret_cast<const f32x4 *>(A.gbar) + 2 * vec;
+          const f32x4 ga = __builtin_nontemporal_load(g4), gb = __builtin_nontemporal_load(g4 + 1);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) { g[e] = ga[e]; g[e + 4] = gb[e]; }
+        } else {
+#pragma unroll
+          for (int e = 0; e < kVec; ++e) g[e] = e < nvalid ? A.gbar[e0 + e] : 0.0f;
+        }
+      } else {
+        reduce_average(A.rows, A.avg, vec, nvalid, g);
+      }
+#pragma unroll
+      for (int e = 0; e < kVec; ++e) {
+        adam(coef * static_cast<double>(g[e]), th[e], mo[e], va[e], A.k);
+      }
+    }
+    unsigned pb[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      pb[e] = pack_bf16(th[2 * e], th[2 * e + 1]);
+      p[2 * e] = bf16_lo(pb[e]);
+      p[2 * e + 1] = bf16_hi(pb[e]);
+    }
+    if (nvalid == kVec) {
+      f32x4 *t4 = reinterpret_cast<f32x4 *>(A.master) + 2 * vec;
+      f32x4 *m4 = reinterpret_cast<f32x4 *>(A.m) + 2 * vec;
+      f32x4 *v4 = reinterpret_cast<f32x4 *>(A.v) + 2 * vec;
+      f32x4 o[6];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        o[0][e] = th[e]; o[1][e] = th[e + 4];
+        o[2][e] = mo[e]; o[3][e] = mo[e + 4];
+        o[4][e] = va[e]; o[5][e] = va[e + 4];
+      }
+      t4[0] = o[0]; t4[1] = o[1];
+      m4[0] = o[2]; m4[1] = o[3];
+      v4[0] = o[4]; v4[1] = o[5];
+      u32x4 pv;
+      pv.x = pb[0]; pv.y = pb[1]; pv.z = pb[2]; pv.w = pb[3];
+      __builtin_nontemporal_store(pv, reinterpret_cast<u32x4 *>(A.pout) + vec);
+    } else if (nvalid > 0) {
+#pragma unroll
+      for (int e = 0; e < kVec; ++e) {
+        if (e < nvalid) {
+          A.master[e0 + e] = th[e];
+          A.m[e0 + e] = mo[e];
+          A.v[e0 + e] = va[e];
+          A.pout[e0 + e] = static_cast<uint16_t>(pb[e / 2] >> (16 * (e & 1)));
+        }
+      }
+    }
+    if constexpr (QL > 0) quant_lane<QL>(p, nvalid, vec, A.codes, A.scales);
+  }
+}
+
+// a2, first kernel: block partial sums of gbar^2 (binary64).  The grid is
+// fixed by n alone; each block's partial is a fixed-order reduction.
+__global__ void __launch_bounds__(kThreads) gnorm_partial_kernel(const NormArgs A) {
+  const int64_t nvec = (A.n + kVec - 1) / kVec;
+  const int64_t stride = int64_t(gridDim.x) * kThreads;
+  double acc = 0.0;
+  for (int64_t vec = int64_t(blockIdx.x) * kThreads + threadIdx.x; vec < nvec; vec += stride) {
+    const int64_t e0 = vec * kVec;
+    const int nvalid = e0 + kVec <= A.n ? kVec : int(A.n - e0);
+    float g[kVec];
+    reduce_average(A.rows, A.avg, vec, nvalid, g);
+    if (A.gbar_out) {
+      if (nvalid == kVec) {
+        f32x4 a, b;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) { a[e] = g[e]; b[e] = g[e + 4]; }
+        f32x4 *o = reinterpret_cast<f32x4 *>(A.gbar_out) + 2 * vec;
+        o[0] = a;
+        o[1] = b;
+      } else {
+#pragma unroll
+        for (int e = 0; e < kVec; ++e)
+          if (e < nvalid) A.gbar_out[e0 + e] = g[e];
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < kVec; ++e) {
+      if (e < nvalid) {
+        const double x = static_cast<double>(g[e]);
+        acc += x * x;
+      }
+    }
+  }
+  // wave: butterfly over 64 lanes; block: the 4 wave sums in wave order
+  for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
+  __shared__ double wsum[kThreads / 64];
+  if ((threadIdx.x & 63) == 0) wsum[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double s = 0.0;
+    for (int w = 0; w < kThreads / 64; ++w) s += wsum[w];
+    A.partials[blockIdx.x] = s;
+  }
+}
+
+// a2, second kernel: one block reduces the partials in a fixed order.
+__global__ void __launch_bounds__(kThreads) gnorm_final_kernel(const double *partials, int np,
+                                                               double *out) {
+  __shared__ double buf[kThreads];
+  double s = 0.0;
+  for (int i = threadIdx.x; i < np; i += kThreads) s += partials[i];
+  buf[threadIdx.x] = s;
+  __syncthreads();
+  for (int half = kThreads / 2; half >= 1; half >>= 1) {
+    if (threadIdx.x < half) buf[threadIdx.x] += buf[threadIdx.x + half];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) *out = buf[0];
+}
+
+// a5 as its own pass over the bf16 shard.
+template <int QL>
+__global__ void __launch_bounds__(kThreads) quant_kernel(const QuantArgs A) {
+  const int lane = threadIdx.x & 63;
+  const int64_t nvec = (A.n + kVec - 1) / kVec;
+  const int64_t stride = int64_t(gridDim.x) * kThreads;
+  for (int64_t base = int64_t(blockIdx.x) * kThreads + (threadIdx.x & ~63); base < nvec;
+       base += stride) {
+    const int64_t vec = base + lane;
+    const int64_t e0 = vec * kVec;
+    const int nvalid = e0 + kVec <= A.n ? kVec : (e0 < A.n ? int(A.n - e0) : 0);
+    float p[kVec];
+    if (nvalid == kVec) {
+      const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(A.p) + vec);
+      p[0] = bf16_lo(w.x); p[1] = bf16_hi(w.x); p[2] = bf16_lo(w.y); p[3] = bf16_hi(w.y);
+      p[4] = bf16_lo(w.z); p[5] = bf16_hi(w.z); p[6] = bf16_lo(w.w); p[7] = bf16_hi(w.w);
+    } else {
+#pragma unroll
+      for (int e = 0; e < kVec; ++e)
+        p[e] = e < nvalid ? __uint_as_float(unsigned(A.p[e0 + e]) << 16) : 0.0f;
+    }
+    quant_lane<QL>(p, nvalid, vec, A.codes, A.scales);
+  }
+}
+
+// --------------------------------------------------------------- host side
+
+constexpr uint32_t kMagic = 0x5a534831u;
+
+}  // namespace
+
+struct zs_handle {
+  uint32_t magic;
+  zs_desc d;
+  int device;
+  int cus;
+  double *partials;   // kNormBlocks fp64, library-owned scratch
+  bool spill_valid;   // gbar_ws holds the gradient of the pending step
+};
+
+namespace {
+
+std::mutex g_live_mu;
+std::unordered_set<zs_handle *> g_live;
+
+bool live(zs_handle *h) {
+  std::lock_guard<std::mutex> lk(g_live_mu);
+  return h && g_live.count(h) && h->magic == kMagic;
+}
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool is_finite(double x) { return std::isfinite(x); }
+
+int quant_lanes(int32_t block) {
+  switch (block) {
+    case 32: return 4;
+    case 64: return 8;
+    case 128: return 16;
+    case 256: return 32;
+    case 512: return 64;
+    default: return -1;
+  }
+}
+
+int64_t grid_blocks(const zs_handle *h, int64_t nvec) {
+  int64_t need = (nvec + kThreads - 1) / kThreads;
+  if (need < 1) need = 1;
+  int64_t per_cu = ZS_BLOCKS_PER_CU;
+  if (const char *e = std::getenv("ZS_BLOCKS_PER_CU")) per_cu = std::atoll(e);
+  if (per_cu <= 0) return need > 0x7fffffff ? 0x7fffffff : need;  // one lane-vector per lane
+  const int64_t cap = int64_t(h->cus) * per_cu;
+  return need < cap ? need : cap;
+}
+
+Avg make_avg(int32_t nd) {
+  Avg a;
+  a.nd = nd;
+  a.pow2 = (nd & (nd - 1)) == 0;
+  a.nd_f = double(nd);
+  a.inv_nd = 1.0 / double(nd);
+  return a;
+}
+
+int check_rows(const zs_handle *h, const zs_bf16 *const *contrib, Rows *rows) {
+  if (!contrib) return ZS_EINVAL;
+  std::memset(rows, 0, sizeof *rows);
+  for (int k = 0; k < h->d.n_d; ++k) {
+    if (!contrib[k]) return ZS_EINVAL;
+    if (!aligned(contrib[k], 16)) return ZS_EALIGN;
+    rows->p[k] = reinterpret_cast<const u32x4 *>(contrib[k]);
+  }
+  return ZS_OK;
+}
+
+int current_device_ok(const zs_handle *h) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return ZS_EHIP;
+  return dev == h->device ? ZS_OK : ZS_EDEVICE;
+}
+
+int launched() { return hipGetLastError() == hipSuccess ? ZS_OK : ZS_EHIP; }
+
+}  // namespace
+
+extern "C" {
+
+int64_t zero_shard_len(int64_t phi, int32_t n_d, int32_t r) {
+  if (phi < 0 || n_d < 1 || r < 0 || r >= n_d) return -1;
+  const int64_t per = phi / n_d + (phi % n_d != 0);
+  const int64_t rest = phi - int64_t(r) * per;
+  if (rest <= 0) return 0;
+  return rest < per ? rest : per;
+}
+
+const char *zero_shard_strerror(int code) {
+  switch (code) {
+    case ZS_OK: return "ok";
+    case ZS_EINVAL: return "invalid argument";
+    case ZS_EALIGN: return "pointer not aligned as required";
+    case ZS_ENOMEM: return "device scratch allocation failed";
+    case ZS_EHIP: return "HIP runtime error or kernel launch failure";
+    case ZS_EDEVICE: return "current device is not the gfx950 the handle was made on";
+    case ZS_ESTATE: return "call out of order or handle not live";
+    default: return "unknown zero_shard status";
+  }
+}
+
+int zero_shard_init(const zs_desc *d, zs_handle **out) {
+  if (!d || !out) return ZS_EINVAL;
+  *out = nullptr;
+  if (d->n_d < 1 || d->n_d > ZS_MAX_ND || d->r < 0 || d->r >= d->n_d || d->phi < 0)
+    return ZS_EINVAL;
+  const int64_t want = zero_shard_len(d->phi, d->n_d, d->r);
+  if (!(d->shard_len == want || (d->r == 0 && d->shard_len == d->phi))) return ZS_EINVAL;
+  if (!(d->beta1 >= 0.0f && d->beta1 < 1.0f && d->beta2 >= 0.0f && d->beta2 < 1.0f))
+    return ZS_EINVAL;
+  if (!(d->eps > 0.0f) || !is_finite(d->eps)) return ZS_EINVAL;
+  if (!(d->weight_decay >= 0.0f) || !is_finite(d->weight_decay)) return ZS_EINVAL;
+  if (d->bias_correction != 0 && d->bias_correction != 1) return ZS_EINVAL;
+  if (!is_finite(d->max_norm)) return ZS_EINVAL;
+  if (d->quant_block != 0 && quant_lanes(d->quant_block) < 0) return ZS_EINVAL;
+  const int64_t n = d->shard_len;
+  if (n > 0) {
+    if (!d->master || !d->m || !d->v || !d->param_out) return ZS_EINVAL;
+    if (!aligned(d->master, 16) || !aligned(d->m, 16) || !aligned(d->v, 16) ||
+        !aligned(d->param_out, 16))
+      return ZS_EALIGN;
+    if (d->quant_block > 0) {
+      if (!d->q_codes || !d->q_scales) return ZS_EINVAL;
+      if (!aligned(d->q_codes, 8) || !aligned(d->q_scales, 4)) return ZS_EALIGN;
+    }
+    if (d->gbar_ws && !aligned(d->gbar_ws, 16)) return ZS_EALIGN;
+  }
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return ZS_EDEVICE;
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return ZS_EHIP;
+  if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) return ZS_EDEVICE;
+  zs_handle *h = new (std::nothrow) zs_handle();
+  if (!h) return ZS_ENOMEM;
+  h->magic = kMagic;
+  h->d = *d;
+  h->device = dev;
+  h->cus = prop.multiProcessorCount > 0 ? prop.multiProcessorCount : 256;
+  h->spill_valid = false;
+  if (hipMalloc(&h->partials, kNormBlocks * sizeof(double)) != hipSuccess) {
+    delete h;
+    return ZS_ENOMEM;
+  }
+  {
+    std::lock_guard<std::mutex> lk(g_live_mu);
+    g_live.insert(h);
+  }
+  *out = h;
+  return ZS_OK;
+}
+
+int zero_shard_gnorm(zs_handle *h, const zs_bf16 *const *contrib, double *sumsq_dev) {
+  if (!live(h)) return ZS_ESTATE;
+  if (!sumsq_dev) return ZS_EINVAL;
+  if (!aligned(sumsq_dev, 8)) return ZS_EALIGN;
+  const int64_t n = h->d.shard_len;
+  NormArgs A;
+  std::memset(&A.rows, 0, sizeof A.rows);
+  if (n > 0) {
+    const int rc = check_rows(h, contrib, &A.rows);
+    if (rc) return rc;
+  }
+  int rc = current_device_ok(h);
+  if (rc) return rc;
+  const hipStream_t st = static_cast<hipStream_t>(h->d.stream);
+  const int64_t nvec = (n + kVec - 1) / kVec;
+  int64_t blocks = (nvec + kThreads - 1) / kThreads;
+  if (blocks > kNormBlocks) blocks = kNormBlocks;
+  if (blocks < 1) blocks = 1;
+  A.avg = make_avg(h->d.n_d);
+  A.n = n;
+  A.gbar_out = h->d.gbar_ws;
+  A.partials = h->partials;
+  hipLaunchKernelGGL(gnorm_partial_kernel, dim3(unsigned(blocks)), dim3(kThreads), 0, st, A);
+  if ((rc = launched())) return rc;
+  hipLaunchKernelGGL(gnorm_final_kernel, dim3(1), dim3(kThreads), 0, st,
+                     static_cast<const double *>(h->partials), int(blocks), sumsq_dev);
+  if ((rc = launched())) return rc;
+  h->spill_valid = h->d.gbar_ws != nullptr;
+  return ZS_OK;
+}
+
+int zero_shard_step(zs_handle *h, const zs_bf16 *const *contrib, float lr, int64_t t,
+                    const double *global_sumsq_dev) {
+  if (!live(h)) return ZS_ESTATE;
+  const zs_desc &d = h->d;
+  if (!(lr >= 0.0f) || !is_finite(lr) || t < 1) return ZS_EINVAL;
+  const bool clip = d.max_norm > 0.0f;
+  if (clip && !global_sumsq_dev) return ZS_EINVAL;
+  if (clip && !aligned(global_sumsq_dev, 8)) return ZS_EALIGN;
+  const bool use_spill = clip && d.gbar_ws;
+  if (use_spill && !h->spill_valid) return ZS_ESTATE;
+  const int64_t n = d.shard_len;
+  StepArgs A;
+  std::memset(&A.rows, 0, sizeof A.rows);
+  if (n > 0 && !use_spill) {
+    const int rc = check_rows(h, contrib, &A.rows);
+    if (rc) return rc;
+  }
+  int rc = current_device_ok(h);
+  if (rc) return rc;
+  h->spill_valid = false;
+  if (n == 0) return ZS_OK;
+  A.avg = make_avg(d.n_d);
+  const double b1 = d.beta1, b2 = d.beta2;
+  A.k.b1 = b1;
+  A.k.omb1 = 1.0 - b1;
+  A.k.b2 = b2;
+  A.k.omb2 = 1.0 - b2;
+  A.k.bc1 = d.bias_correction ? 1.0 - std::pow(b1, double(t)) : 1.0;
+  A.k.bc2 = d.bias_correction ? 1.0 - std::pow(b2, double(t)) : 1.0;
+  A.k.lr = double(lr);
+  A.k.decay = double(lr) * double(d.weight_decay);
+  A.k.eps = double(d.eps);
+  A.n = n;
+  A.sumsq = clip ? global_sumsq_dev : nullptr;
+  A.max_norm = double(d.max_norm);
+  A.gbar = use_spill ? d.gbar_ws : nullptr;
+  A.master = d.master;
+  A.m = d.m;
+  A.v = d.v;
+  A.pout = d.param_out;
+  A.codes = d.q_codes;
+  A.scales = d.q_scales;
+  const hipStream_t st = static_cast<hipStream_t>(d.stream);
+  const int64_t nvec = (n + kVec - 1) / kVec;
+  const dim3 grid(unsigned(grid_blocks(h, nvec))), block(kThreads);
+  switch (d.quant_block) {
+    case 0: hipLaunchKernelGGL(step_kernel<0>, grid, block, 0, st, A); break;
+    case 32: hipLaunchKernelGGL(step_kernel<4>, grid, block, 0, st, A); break;
+    case 64: hipLaunchKernelGGL(step_kernel<8>, grid, block, 0, st, A); break;
+    case 128: hipLaunchKernelGGL(step_kernel<16>, grid, block, 0, st, A); break;
+    case 256: hipLaunchKernelGGL(step_kernel<32>, grid, block, 0, st, A); break;
+    case 512: hipLaunchKernelGGL(step_kernel<64>, grid, block, 0, st, A); break;
+    default: return ZS_EINVAL;
+  }
+  return launched();
+}
+
+int zero_shard_quant(zs_handle *h, int32_t block) {
+  if (!live(h)) return ZS_ESTATE;
+  const zs_desc &d = h->d;
+  if (quant_lanes(block) < 0) return ZS_EINVAL;
+  const int64_t n = d.shard_len;
+  if (n > 0) {
+    if (!d.q_codes || !d.q_scales) return ZS_EINVAL;
+    if (!aligned(d.q_codes, 8) || !aligned(d.q_scales, 4)) return ZS_EALIGN;
+  }
+  int rc = current_device_ok(h);
+  if (rc) return rc;
+  if (n == 0) return ZS_OK;
+  QuantArgs A{d.param_out, n, d.q_codes, d.q_scales};
+  const hipStream_t st = static_cast<hipStream_t>(d.stream);
+  const int64_t nvec = (n + kVec - 1) / kVec;
+  const dim3 grid(unsigned(grid_blocks(h, nvec))), blk(kThreads);
+  switch (block) {
+    case 32: hipLaunchKernelGGL(quant_kernel<4>, grid, blk, 0, st, A); break;
+    case 64: hipLaunchKernelGGL(quant_kernel<8>, grid, blk, 0, st, A); break;
+    case 128: hipLaunchKernelGGL(quant_kernel<16>, grid, blk, 0, st, A); break;
+    case 256: hipLaunchKernelGGL(quant_kernel<32>, grid, blk, 0, st, A); break;
+    case 512: hipLaunchKernelGGL(quant_kernel<64>, grid, blk, 0, st, A); break;
+    default: return ZS_EINVAL;
+  }
+  return launched();
+}
+
+int zero_shard_free(zs_handle *h) {
+  if (!h) return ZS_OK;
+  {
+    std::lock_guard<std::mutex> lk(g_live_mu);
+    if (!g_live.count(h)) return ZS_ESTATE;
+    g_live.erase(h);
+  }
+  int rc = ZS_OK;
+  if (hipStreamSynchronize(static_cast<hipStream_t>(h->d.stream)) != hipSuccess) rc = ZS_EHIP;
+  if (hipFree(h->partials) != hipSuccess) rc = ZS_EHIP;
+  h->magic = 0;
+  delete h;
+  return rc;
+}
+
+}  // extern "C"

@@ -1,0 +1,179 @@
+"""GPU-side and oracle-side drivers of a workload, shared by the GPU tests,
+the smoke check and the benchmark's CPU baseline.
+
+``GpuShard`` owns the device tensors of one shard (state, outputs, the
+N_d contribution rows) and calls the library through its C ABI.
+The oracle is imported only by the oracle-side helpers, so the benchmark
+can drive ``GpuShard`` without loading it.  ``OracleWindow`` evolves any window [i0, i0+n) of the same shard on the CPU
+with the oracle; unclipped steps are elementwise, so a window needs only
+its own inputs, and with clipping the caller supplies the global sum of
+squares computed by ``oracle_global_sumsq``.  Inputs on both sides come
+from the seeded generator (device and host builds of one definition).
+"""
+
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+
+import seeded_inputs as S
+import sharded_mixed_precision_zero_amd as Z
+
+DEV = "cuda:0"
+
+
+def log(*a) -> None:
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def row_stride(n: int) -> int:
+    """Elements between contribution rows: 16-byte aligned, and offset by a
+    non-power-of-two amount so rows do not start on the same HBM channel."""
+    return (n + 127) // 128 * 128 + 640
+
+
+class GpuShard:
+    def __init__(self, w: S.Workload, n: int | None = None, i0: int = 0, *, spill: bool = True,
+                 quant_block: int | None = None, n_d: int | None = None, phi: int | None = None,
+                 r: int | None = None, bias_correction: bool = True, stream=None):
+        import torch
+
+        self.torch = torch
+        self.w = w
+        self.n = w.shard_len if n is None else int(n)
+        self.i0 = i0
+        self.nd = w.n_d if n_d is None else n_d
+        self.qb = w.quant_block if quant_block is None else quant_block
+        self.clip = w.max_norm > 0
+        n_ = self.n
+        f32 = dict(dtype=torch.float32, device=DEV)
+        self.master = torch.empty(n_, **f32)
+        self.m = torch.empty(n_, **f32)
+        self.v = torch.empty(n_, **f32)
+        self.p = torch.empty(n_, dtype=torch.int16, device=DEV)
+        self.codes = self.scales = None
+        if self.qb:
+            self.codes = torch.empty(n_, dtype=torch.int8, device=DEV)
+            self.scales = torch.empty((n_ + self.qb - 1) // self.qb, **f32)
+        self.gbar_ws = torch.empty(n_, **f32) if (self.clip and spill) else None
+        self.sumsq = torch.zeros(1, dtype=torch.float64, device=DEV)
+        self.stride = row_stride(n_)
+        self.rows_buf = torch.empty(max(1, (self.nd - 1) * self.stride + n_), dtype=torch.int16,
+                                    device=DEV)
+        self.rows = [self.rows_buf[k * self.stride: k * self.stride + n_] for k in range(self.nd)]
+        if phi is None:
+            phi, r = (w.phi, w.r) if n is None else (n_, 0)
+        self.shard = Z.ZeroShard(
+            phi=phi, n_d=self.nd, r=w.r if r is None else r, shard_len=n_, master=self.master,
+            m=self.m, v=self.v, param_out=self.p, beta1=w.beta1, beta2=w.beta2, eps=w.eps,
+            weight_decay=w.weight_decay, bias_correction=bias_correction,
+            max_norm=w.max_norm, quant_block=self.qb, q_codes=self.codes,
+            q_scales=self.scales, gbar_ws=self.gbar_ws,
+            stream=stream if stream is not None else torch.cuda.current_stream())
+
+    def init_state(self) -> None:
+        S.dev_state(self.w, self.master, self.m, self.v, i0=self.i0)
+
+    def fill_grads(self, s: int) -> None:
+        S.dev_contrib(self.w, s, self.rows_buf, self.n, self.stride, i0=self.i0)
+
+    def step(self, s: int, lr: float | None = None) -> None:
+        """Step s (1-based) on the resident contributions."""
+        lr = self.w.lr if lr is None else lr
+        if self.clip:
+            self.shard.gnorm(self.rows, self.sumsq)
+            self.shard.step(None if self.gbar_ws is not None else self.rows, lr,
+                            self.w.t_of(s), self.sumsq)
+        else:
+            self.shard.step(self.rows, lr, self.w.t_of(s))
+
+    def host(self, lo: int = 0, hi: int | None = None) -> dict:
+        hi = self.n if hi is None else hi
+        out = {
+            "master": self.master[lo:hi].cpu().numpy(),
+            "m": self.m[lo:hi].cpu().numpy(),
+            "v": self.v[lo:hi].cpu().numpy(),
+            "p": self.p[lo:hi].cpu().numpy().view(np.uint16),
+        }
+        if self.qb:
+            out["codes"] = self.codes[lo:hi].cpu().numpy()
+            assert lo % self.qb == 0
+            out["scales"] = self.scales[lo // self.qb:(hi + self.qb - 1) // self.qb].cpu().numpy()
+        return out
+
+    def free(self) -> None:
+        self.shard.free()
+
+
+class OracleWindow:
+    """Oracle state of shard elements [i0, i0+n) of workload w."""
+
+    def __init__(self, w: S.Workload, i0: int, n: int, threads: int = 16,
+                 bias_correction: bool = True):
+        import oracle
+
+        self.O = oracle
+        self.w, self.i0, self.n, self.threads = w, int(i0), int(n), threads
+        self.bias_correction = int(bool(bias_correction))
+        self.master, self.m, self.v = S.host_state(w, i0, n)
+        self.last = None
+
+    def hyper(self, s: int):
+        w = self.w
+        return self.O.Hyper(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps,
+                       weight_decay=w.weight_decay, t=w.t_of(s),
+                       bias_correction=self.bias_correction)
+
+    def step(self, s: int, sumsq_total: float | None = None):
+        O = self.O
+        rows = list(S.host_contrib(self.w, s, self.i0, self.n))
+        h = self.hyper(s)
+        if self.w.max_norm > 0:
+            assert sumsq_total is not None
+            gbar = O.reduce_average(rows)
+            coef = O.clip_coef(sumsq_total, self.w.max_norm)
+            O.adam(self.master, self.m, self.v, gbar, coef, h)
+            p = O.f32_to_bf16(self.master)
+            codes = scales = None
+            if self.w.quant_block:
+                codes, scales = O.quant_int8(p, self.w.quant_block)
+            self.last = O.StepOut(p, codes, scales, O.sumsq(gbar))
+        else:
+            h.quant_block = self.w.quant_block
+            self.last = O.step(rows, self.master, self.m, self.v, h, threads=self.threads)
+        return self.last
+
+
+def oracle_global_sumsq(w: S.Workload, s: int, chunk: int = 1 << 23, threads: int = 16) -> float:
+    """Sum of squares of the averaged gradient over the whole shard at step
+    s, streamed through the host in chunks combined in chunk order."""
+    import oracle as O
+
+    total = 0.0
+    for lo in range(0, w.shard_len, chunk):
+        n = min(chunk, w.shard_len - lo)
+        rows = S.host_contrib(w, s, lo, n)
+        _, part = O.gbar_sumsq(list(rows), threads=threads)
+        total += part
+    return total
+
+
+def windows(n: int, count: int, size: int, seed: int, extra: tuple = ()) -> list[tuple[int, int]]:
+    """Disjoint windows [lo, hi) of about `size` elements: the head, the tail
+    (running to n), windows at the `extra` anchor points and at seeded
+    offsets.  Every window starts on a multiple of 256 elements."""
+    size = min(size, n)
+    last = (n - size) // 256 * 256
+    anchors = [0, last] + [int(a) for a in extra]
+    rng = np.random.default_rng(seed)
+    while len(anchors) < count:
+        anchors.append(int(rng.integers(0, max(1, n - size))))
+    out = []
+    for a in anchors:
+        lo = min(max(0, a), last) // 256 * 256
+        hi = n if lo == last else min(n, lo + size)
+        if all(hi <= l2 or lo >= h2 for l2, h2 in out):
+            out.append((lo, hi))
+    return sorted(out)

@@ -1,0 +1,78 @@
+"""Comparison rules of the parity tests (GPU result vs oracle).
+
+* fp32 master, m, v: |gpu - oracle| <= 1e-9 + 2e-6 |oracle| element by
+  element (NaN matches NaN);
+* bf16 parameters: at most 1 apart in the ordered sequence of bf16 patterns
+  (+0 and -0 count as equal);
+* int8 codes and fp32 scales: equal bit for bit, on every block whose bf16
+  input is bit-identical on both sides.  A block whose input differs (by the
+  allowed 1 ulp) has another correct quantization; there the GPU's codes
+  must be those of the GPU's own bf16 block, which the caller checks with
+  the stand-alone quantizer.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+RTOL = 2e-6
+ATOL = 1e-9
+
+
+def f32_close(name: str, gpu: np.ndarray, orc: np.ndarray, rtol: float = RTOL,
+              atol: float = ATOL) -> dict:
+    assert gpu.shape == orc.shape and gpu.dtype == np.float32 and orc.dtype == np.float32
+    g, o = gpu.astype(np.float64), orc.astype(np.float64)
+    both_nan = np.isnan(g) & np.isnan(o)
+    with np.errstate(invalid="ignore"):
+        ok = (np.abs(g - o) <= atol + rtol * np.abs(o)) | both_nan
+    if not ok.all():
+        i = int(np.flatnonzero(~ok)[0])
+        raise AssertionError(f"{name}: {int((~ok).sum())} of {ok.size} out of tolerance; "
+                             f"first at {i}: gpu={gpu[i]!r} oracle={orc[i]!r}")
+    same = gpu.view(np.uint32) == orc.view(np.uint32)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        rel = np.where(o != 0, np.abs(g - o) / np.abs(o), 0.0)
+    return {"bitwise": float(same.mean()), "max_rel": float(np.nanmax(rel)) if rel.size else 0.0}
+
+
+def _bf16_order(b: np.ndarray) -> np.ndarray:
+    b = b.astype(np.int32)
+    return np.where(b & 0x8000, -(b & 0x7FFF), b)
+
+
+def bf16_close(name: str, gpu: np.ndarray, orc: np.ndarray, max_ulp: int = 1) -> dict:
+    gpu, orc = gpu.view(np.uint16), orc.view(np.uint16)
+    assert gpu.shape == orc.shape
+    nan_g = ((gpu & 0x7F80) == 0x7F80) & ((gpu & 0x7F) != 0)
+    nan_o = ((orc & 0x7F80) == 0x7F80) & ((orc & 0x7F) != 0)
+    d = np.abs(_bf16_order(gpu) - _bf16_order(orc))
+    ok = ((d <= max_ulp) & ~nan_g & ~nan_o) | (nan_g & nan_o)
+    if not ok.all():
+        i = int(np.flatnonzero(~ok)[0])
+        raise AssertionError(f"{name}: {int((~ok).sum())} of {ok.size} more than {max_ulp} ulp "
+                             f"apart; first at {i}: gpu=0x{gpu[i]:04x} oracle=0x{orc[i]:04x}")
+    return {"bitwise": float((gpu == orc).mean())}
+
+
+def int8_exact(name: str, gpu_codes: np.ndarray, gpu_scales: np.ndarray, orc_codes: np.ndarray,
+               orc_scales: np.ndarray, gpu_p: np.ndarray, orc_p: np.ndarray, block: int) -> np.ndarray:
+    """Exact equality on blocks with identical bf16 input; returns the mask
+    of blocks whose input differs (to be checked against the stand-alone
+    quantizer)."""
+    n = gpu_p.size
+    nb = (n + block - 1) // block
+    pad = nb * block - n
+    diff = np.concatenate([gpu_p.view(np.uint16) != orc_p.view(np.uint16),
+                           np.zeros(pad, bool)]).reshape(nb, block).any(axis=1)
+    same_blk = ~diff
+    cg = np.concatenate([gpu_codes, np.zeros(pad, np.int8)]).reshape(nb, block)
+    co = np.concatenate([orc_codes, np.zeros(pad, np.int8)]).reshape(nb, block)
+    bad_codes = (cg != co).any(axis=1) & same_blk
+    both_nan = np.isnan(gpu_scales) & np.isnan(orc_scales)
+    bad_scales = (gpu_scales.view(np.uint32) != orc_scales.view(np.uint32)) & same_blk & ~both_nan
+    if bad_codes.any() or bad_scales.any():
+        b = int(np.flatnonzero(bad_codes | bad_scales)[0])
+        raise AssertionError(f"{name}: block {b} differs with identical input "
+                             f"({int(bad_codes.sum())} code blocks, {int(bad_scales.sum())} scales)")
+    return diff

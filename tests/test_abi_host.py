@@ -1,0 +1,135 @@
+"""The C ABI on the CPU: the library loads, exports every declared symbol,
+matches the header's struct layout, and rejects bad arguments before it
+touches a device.  No kernel is launched here."""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+import subprocess
+import tempfile
+
+import pytest
+
+import seeded_inputs as S
+import sharded_mixed_precision_zero_amd as Z
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "zero_shard.h")
+
+
+def _declared_functions() -> list[str]:
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(zero_shard_\w+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = _declared_functions()
+    assert set(names) == set(Z.EXPORTS)
+    lib = ctypes.CDLL(Z.LIB_PATH)
+    for nm in names:
+        assert hasattr(lib, nm), nm
+    # and the shared object's dynamic symbol table lists them
+    out = subprocess.run(["nm", "-D", "--defined-only", Z.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    for nm in names:
+        assert re.search(rf"\bT {nm}$", out, flags=re.M), nm
+
+
+def test_descriptor_layout_matches_header():
+    fields = [f for f, _ in Z.zs_desc._fields_]
+    prog = ["#include <stddef.h>", "#include <stdio.h>", '#include "zero_shard.h"',
+            "int main(void) {", 'printf("size %zu\\n", sizeof(zs_desc));']
+    prog += [f'printf("{f} %zu\\n", offsetof(zs_desc, {f}));' for f in fields]
+    prog += ["return 0; }"]
+    with tempfile.TemporaryDirectory() as d:
+        src, exe = os.path.join(d, "l.c"), os.path.join(d, "l")
+        open(src, "w").write("\n".join(prog))
+        subprocess.run(["gcc", "-std=c99", "-I", os.path.dirname(HEADER), src, "-o", exe],
+                       check=True)
+        out = subprocess.run([exe], capture_output=True, text=True, check=True).stdout
+    got = dict(line.split() for line in out.strip().splitlines())
+    assert int(got.pop("size")) == ctypes.sizeof(Z.zs_desc)
+    for f in fields:
+        assert int(got[f]) == getattr(Z.zs_desc, f).offset, f
+
+
+def test_partition_geometry():
+    for w in S.WORKLOADS:
+        assert Z.zero_shard_len(w.phi, w.n_d, w.r) == w.shard_len
+    # uneven: ceil(phi/n_d) per shard, the last one shorter, empty past phi
+    assert [Z.zero_shard_len(10, 4, r) for r in range(4)] == [3, 3, 3, 1]
+    assert [Z.zero_shard_len(3, 4, r) for r in range(4)] == [1, 1, 1, 0]
+    assert sum(Z.zero_shard_len(1_000_003, 7, r) for r in range(7)) == 1_000_003
+    assert Z.zero_shard_len(0, 1, 0) == 0
+    for bad in [(-1, 4, 0), (10, 0, 0), (10, 4, 4), (10, 4, -1)]:
+        assert Z.zero_shard_len(*bad) == -1
+
+
+def test_strerror():
+    for c in (0, -1, -2, -3, -4, -5, -6):
+        assert Z.zero_shard_strerror(c)
+    assert "unknown" in Z.zero_shard_strerror(-99)
+
+
+def _desc(**kw) -> Z.zs_desc:
+    base = dict(phi=4096, n_d=4, r=1, shard_len=1024, beta1=0.9, beta2=0.999, eps=1e-8,
+                weight_decay=0.0, bias_correction=1, max_norm=0.0, quant_block=0,
+                master=0x10000, m=0x20000, v=0x30000, param_out=0x40000, q_codes=None,
+                q_scales=None, gbar_ws=None, stream=None)
+    base.update(kw)
+    return Z.zs_desc(**base)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(n_d=0), Z.ZS_EINVAL),
+    (dict(n_d=65, r=0, shard_len=64), Z.ZS_EINVAL),
+    (dict(r=4), Z.ZS_EINVAL),
+    (dict(r=-1), Z.ZS_EINVAL),
+    (dict(shard_len=1000), Z.ZS_EINVAL),
+    (dict(phi=-5), Z.ZS_EINVAL),
+    (dict(beta1=1.0), Z.ZS_EINVAL),
+    (dict(beta2=-0.1), Z.ZS_EINVAL),
+    (dict(eps=0.0), Z.ZS_EINVAL),
+    (dict(eps=float("inf")), Z.ZS_EINVAL),
+    (dict(weight_decay=-1.0), Z.ZS_EINVAL),
+    (dict(bias_correction=2), Z.ZS_EINVAL),
+    (dict(max_norm=float("nan")), Z.ZS_EINVAL),
+    (dict(quant_block=100), Z.ZS_EINVAL),
+    (dict(quant_block=256), Z.ZS_EINVAL),            # codes/scales missing
+    (dict(master=None), Z.ZS_EINVAL),
+    (dict(param_out=None), Z.ZS_EINVAL),
+    (dict(master=0x10004), Z.ZS_EALIGN),
+    (dict(v=0x30008), Z.ZS_EALIGN),
+    (dict(param_out=0x40002), Z.ZS_EALIGN),
+    (dict(quant_block=256, q_codes=0x50004, q_scales=0x60000), Z.ZS_EALIGN),
+    (dict(gbar_ws=0x70004), Z.ZS_EALIGN),
+])
+def test_init_rejects_bad_descriptors(kw, code):
+    rc, h = Z.zero_shard_init(_desc(**kw))
+    assert rc == code and not h.value
+
+
+def test_calls_on_dead_handles_are_refused():
+    assert Z.zero_shard_step(None, None, 1e-3, 1) == Z.ZS_ESTATE
+    assert Z.zero_shard_gnorm(None, None, None) == Z.ZS_ESTATE
+    assert Z.zero_shard_quant(None, 256) == Z.ZS_ESTATE
+    assert Z.zero_shard_free(None) == Z.ZS_OK
+    fake = ctypes.c_void_p(0x1234560)
+    assert Z.zero_shard_step(fake, None, 1e-3, 1) == Z.ZS_ESTATE
+    assert Z.zero_shard_free(fake) == Z.ZS_ESTATE
+
+
+def test_valid_descriptor_needs_the_gpu():
+    """With no GPU present a valid descriptor gets as far as the device check."""
+    import torch
+
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present; covered by the GPU tests")
+    rc, h = Z.zero_shard_init(_desc())
+    assert rc == Z.ZS_EDEVICE and not h.value
+    rc, h = Z.zero_shard_init(_desc(phi=3, n_d=4, r=3, shard_len=0, master=None, m=None,
+                                    v=None, param_out=None))
+    assert rc == Z.ZS_EDEVICE

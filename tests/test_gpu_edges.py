@@ -1,0 +1,267 @@
+"""GPU edge cases: ragged and degenerate shards, non-power-of-two N_d, every
+quantizer block, clipping on and off, bias correction off, empty shards,
+non-finite inputs, determinism, shard concatenation, checkpoint/resume and
+the error paths of the C ABI.  All against the oracle on seeded inputs, to
+the same tolerances as the workload parity tests."""
+
+from __future__ import annotations
+
+import dataclasses
+
+import numpy as np
+import pytest
+
+import oracle as O
+import seeded_inputs as S
+import sharded_mixed_precision_zero_amd as Z
+from tests import _parity as P
+from tests._gpu import GpuShard, OracleWindow, log
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _gpu_cleanup():
+    import torch
+
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    yield
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def _variant(base: str, **kw) -> S.Workload:
+    return dataclasses.replace(S.by_name(base), **kw)
+
+
+def _run_pair(w: S.Workload, n: int, steps: int, *, bias_correction=True, spill=True,
+              poison=None):
+    """Run `steps` steps of workload w over an n-element unpartitioned shard on
+    the GPU and on the oracle; compare every step."""
+    import torch
+
+    g = GpuShard(w, n=n, spill=spill, bias_correction=bias_correction)
+    g.init_state()
+    ow = OracleWindow(w, 0, n, bias_correction=bias_correction)
+    for s in range(1, steps + 1):
+        g.fill_grads(s)
+        rows_h = S.host_contrib(w, s, 0, n)
+        if poison is not None:
+            k, i, bits = poison
+            g.rows[k][i] = bits - 0x10000 if bits >= 0x8000 else bits
+            rows_h[k, i] = bits
+        g.step(s)
+        torch.cuda.synchronize()
+        h = ow.hyper(s)
+        if w.max_norm > 0:
+            gbar, ssq = O.gbar_sumsq(list(rows_h))
+            coef = O.clip_coef(ssq, w.max_norm)
+            O.adam(ow.master, ow.m, ow.v, gbar, coef, h)
+            p = O.f32_to_bf16(ow.master)
+            codes = scales = None
+            if w.quant_block:
+                codes, scales = O.quant_int8(p, w.quant_block)
+            o = O.StepOut(p, codes, scales, ssq)
+        else:
+            h.quant_block = w.quant_block
+            o = O.step(list(rows_h), ow.master, ow.m, ow.v, h)
+        got = g.host()
+        P.f32_close(f"step {s} master", got["master"], ow.master)
+        P.f32_close(f"step {s} m", got["m"], ow.m)
+        P.f32_close(f"step {s} v", got["v"], ow.v)
+        P.bf16_close(f"step {s} bf16", got["p"], o.p)
+        if w.quant_block:
+            diff = P.int8_exact(f"step {s} int8", got["codes"], got["scales"], o.codes, o.scales,
+                                got["p"], o.p, w.quant_block)
+            if diff.any():  # other correct codes: those of the GPU's own bf16
+                c2, s2 = O.quant_int8(got["p"], w.quant_block)
+                blk = np.repeat(diff, w.quant_block)[:n]
+                assert np.array_equal(got["codes"][blk], c2[blk])
+                assert np.array_equal(np.isnan(got["scales"][diff]), np.isnan(s2[diff]))
+    return g, ow
+
+
+CASES = [
+    # (base workload, n, n_d, quant block, clip)
+    ("tiny-zero1", 1, 1, 0, 0.0),
+    ("tiny-zero1", 7, 3, 32, 0.0),
+    ("tiny-zero1", 9, 64, 0, 1.0),
+    ("tiny-zero1", 255, 4, 256, 1.0),
+    ("tiny-zero1", 257, 6, 64, 0.0),
+    ("tiny-zero1", 4099, 48, 512, 0.05),
+    ("gpt2-small-flat", 65536 + 13, 8, 128, 0.0),
+    ("13B-nd16-clip-int8", 300_001, 16, 256, 1.0),
+    ("7.5B-nd64", 20_000 + 4, 64, 0, 0.0),
+]
+
+
+@pytest.mark.parametrize("base,n,nd,qb,clip", CASES)
+def test_ragged_shapes(base, n, nd, qb, clip):
+    log(f"case {base} n={n} n_d={nd} block={qb} clip={clip}")
+    w = _variant(base, n_d=nd, quant_block=qb, max_norm=clip,
+                 weight_decay=0.1 if clip else 0.0)
+    g, _ = _run_pair(w, n, 3)
+    g.free()
+
+
+def test_clip_without_spill_and_bias_correction_off():
+    log("case clip re-read path, bias correction off")
+    w = _variant("13B-nd16-clip-int8", max_norm=0.01)
+    g, _ = _run_pair(w, 50_000 + 5, 3, spill=False, bias_correction=False)
+    g.free()
+
+
+def test_empty_shard():
+    import torch
+
+    w = S.by_name("tiny-zero1")
+    g = GpuShard(w, n=0, phi=3, r=3)
+    g.sumsq.fill_(123.0)
+    g.shard.gnorm(g.rows, g.sumsq)
+    g.shard.step(g.rows, 1e-3, 1)
+    torch.cuda.synchronize()
+    assert g.sumsq.item() == 0.0
+    g.free()
+
+
+def test_nonfinite_propagates_per_element_unclipped():
+    """A NaN in one contribution element makes exactly that element NaN."""
+    log("case NaN in rank 2, element 1000, unclipped, block 256")
+    w = _variant("tiny-zero1", quant_block=256)
+    g, ow = _run_pair(w, 5000, 2, poison=(2, 1000, 0x7FC0))
+    got = g.host()
+    bad = np.isnan(got["master"])
+    assert bad.sum() == 1 and bad[1000]
+    assert np.isnan(got["scales"][1000 // 256]) and not np.isnan(np.delete(got["scales"], 3)).any()
+    g.free()
+
+
+def test_nonfinite_in_clipped_norm():
+    log("case +Inf in rank 0 element 17, clipped")
+    w = _variant("13B-nd16-clip-int8", quant_block=0)
+    g, ow = _run_pair(w, 3000, 1, poison=(0, 17, 0x7F80))
+    got = g.host()
+    # S = inf -> coef = 0: every other element gets g = 0; element 17 gets inf*0 = NaN
+    assert np.isnan(got["master"][17])
+    assert np.isfinite(np.delete(got["master"], 17)).all()
+    g.free()
+
+
+def test_determinism_bitwise():
+    import torch
+
+    w = _variant("13B-nd16-clip-int8", max_norm=0.5)
+    outs = []
+    for _ in range(2):
+        g = GpuShard(w, n=1_000_003)
+        g.init_state()
+        ss = []
+        for s in range(1, 4):
+            g.fill_grads(s)
+            g.step(s)
+            torch.cuda.synchronize()
+            ss.append(g.sumsq.item())
+        outs.append((g.host(), ss))
+        g.free()
+    a, b = outs
+    assert a[1] == b[1]
+    for k in a[0]:
+        assert np.array_equal(a[0][k].view(np.uint8), b[0][k].view(np.uint8)), k
+
+
+@pytest.mark.parametrize("qb", [0, 256])
+def test_shard_concatenation_bitwise(qb):
+    """Updating the N_d partitions separately and concatenating equals the
+    unpartitioned update (elementwise independence of the optimizer state)."""
+    import torch
+
+    w = _variant("tiny-zero1", quant_block=qb)
+    phi = 4 * 256 * 100 if qb else 4 * 25_000 + 3
+    whole = GpuShard(w, n=phi)
+    whole.init_state()
+    parts = []
+    for r in range(w.n_d):
+        ln = Z.zero_shard_len(phi, w.n_d, r)
+        lo = r * Z.zero_shard_len(phi, w.n_d, 0)
+        parts.append(GpuShard(w, n=ln, i0=lo, phi=phi, r=r))
+        parts[-1].init_state()
+    for s in range(1, 4):
+        whole.fill_grads(s)
+        whole.step(s)
+        for pt in parts:
+            pt.fill_grads(s)
+            pt.step(s)
+    torch.cuda.synchronize()
+    a = whole.host()
+    bs = [pt.host() for pt in parts]
+    for k in a:
+        assert np.array_equal(np.concatenate([b[k] for b in bs]).view(np.uint8),
+                              a[k].view(np.uint8)), k
+    for x in [whole] + parts:
+        x.free()
+
+
+def test_checkpoint_resume_bitwise():
+    """(theta, m, v, t) is the whole state: 6 steps straight equal 3 steps,
+    a save/restore through host memory into a new handle, and 3 more."""
+    import torch
+
+    w = _variant("gpt2-small-flat", quant_block=256)
+    n = 200_000
+    g = GpuShard(w, n=n)
+    g.init_state()
+    for s in range(1, 7):
+        g.fill_grads(s)
+        g.step(s)
+    straight = g.host()
+    g.free()
+    g = GpuShard(w, n=n)
+    g.init_state()
+    for s in range(1, 4):
+        g.fill_grads(s)
+        g.step(s)
+    saved = {k: g.host()[k].copy() for k in ("master", "m", "v")}
+    g.free()
+    torch.cuda.empty_cache()
+    g = GpuShard(w, n=n)
+    g.master.copy_(torch.from_numpy(saved["master"]))
+    g.m.copy_(torch.from_numpy(saved["m"]))
+    g.v.copy_(torch.from_numpy(saved["v"]))
+    for s in range(4, 7):
+        g.fill_grads(s)
+        g.step(s)
+    resumed = g.host()
+    g.free()
+    for k in straight:
+        assert np.array_equal(straight[k].view(np.uint8), resumed[k].view(np.uint8)), k
+
+
+def test_error_paths_leave_outputs_untouched():
+    import torch
+
+    w = S.by_name("13B-nd16-clip-int8")
+    g = GpuShard(w, n=4096)
+    g.init_state()
+    g.fill_grads(1)
+    torch.cuda.synchronize()
+    before = g.host()
+    h = g.shard.h
+    # spill not written yet
+    assert Z.zero_shard_step(h, None, 1e-3, 1, g.sumsq) == Z.ZS_ESTATE
+    # clipping needs S
+    assert Z.zero_shard_step(h, g.rows, 1e-3, 1, None) == Z.ZS_EINVAL
+    for lr, t in [(-1.0, 1), (float("nan"), 1), (1e-3, 0)]:
+        assert Z.zero_shard_step(h, g.rows, lr, t, g.sumsq) == Z.ZS_EINVAL
+    bad_rows = list(g.rows)
+    bad_rows[3] = g.rows_buf[3 * g.stride + 1: 3 * g.stride + 1 + g.n]
+    assert Z.zero_shard_gnorm(h, bad_rows, g.sumsq) == Z.ZS_EALIGN
+    missing = list(g.rows[:-1])
+    assert Z.zero_shard_gnorm(h, missing + [None], g.sumsq) == Z.ZS_EINVAL
+    assert Z.zero_shard_quant(h, 100) == Z.ZS_EINVAL
+    torch.cuda.synchronize()
+    after = g.host()
+    for k in before:
+        assert np.array_equal(before[k].view(np.uint8), after[k].view(np.uint8)), k
+    g.free()
+    assert Z.zero_shard_step(h, g.rows, 1e-3, 1, g.sumsq) == Z.ZS_ESTATE
