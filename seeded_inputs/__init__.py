@@ -51,6 +51,8 @@ def host_lib() -> ctypes.CDLL:
 def dev_lib() -> ctypes.CDLL:
     global _dev
     if _dev is None:
+        import torch  # noqa: F401  (share torch's HIP runtime, see the binding)
+
         if not os.path.exists(DEV_LIB):
             raise RuntimeError(f"generator not built: {DEV_LIB} (run __graft_entry__.build())")
         L = ctypes.CDLL(DEV_LIB)

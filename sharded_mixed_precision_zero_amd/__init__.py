@@ -24,6 +24,12 @@ QUANT_BLOCKS = (32, 64, 128, 256, 512)
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() (hipcc, gfx950)")
 
+# The library must run on the same HIP runtime as the PyTorch that owns the
+# device memory and streams.  Loading torch first makes the library's
+# libamdhip64.so.7 dependency resolve to torch's already-loaded runtime;
+# the other order would map a second runtime into the process.
+import torch  # noqa: E402,F401
+
 _lib = ctypes.CDLL(LIB_PATH)
 
 

@@ -8,6 +8,7 @@ import ctypes
 import os
 import re
 import subprocess
+import sys
 import tempfile
 
 import pytest
@@ -133,3 +134,17 @@ def test_valid_descriptor_needs_the_gpu():
     rc, h = Z.zero_shard_init(_desc(phi=3, n_d=4, r=3, shard_len=0, master=None, m=None,
                                     v=None, param_out=None))
     assert rc == Z.ZS_EDEVICE
+
+
+def test_one_hip_runtime_in_process():
+    """The library binds to the HIP runtime of the PyTorch that owns the
+    memory: importing the binding must not map a second libamdhip64."""
+    code = ("import sys; sys.path.insert(0, %r)\n"
+            "import sharded_mixed_precision_zero_amd, seeded_inputs\n"
+            "seeded_inputs.dev_lib()\n"
+            "import torch\n"
+            "maps = {l.split()[-1] for l in open('/proc/self/maps') if 'libamdhip64' in l}\n"
+            "print(len(maps)); print(maps)\n") % ROOT
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True,
+                         check=True).stdout
+    assert out.splitlines()[0] == "1", out
