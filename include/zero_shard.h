@@ -45,7 +45,7 @@
  * Layouts are flat, contiguous, element i at offset i.  fp32 and bf16
  * arrays and every contribution row must be 16-byte aligned; q_codes 8-byte
  * aligned.  The library owns only the handle and a small device scratch
- * (fp64 block partials of the norm, <= 16 KiB), allocated at init.
+ * (fp64 block partials of the norm, 128 KiB), allocated at init.
  *
  * Errors: every call returns ZS_OK (0) or a negative zs_status.  Arguments
  * are validated before anything is queued: on an error nothing is launched

@@ -46,10 +46,27 @@ constexpr int kVec = 8;          // shard elements per lane
 #ifndef ZS_ROW_GROUP
 #define ZS_ROW_GROUP 8
 #endif
-constexpr int kRowGroup = ZS_ROW_GROUP;  // contribution rows loaded together
-constexpr int kNormBlocks = 2048;        // fixed grid of the norm pass
+constexpr int kRowGroup = ZS_ROW_GROUP;  // contribution rows loaded together (update)
+#ifndef ZS_NORM_ROW_GROUP
+#define ZS_NORM_ROW_GROUP 4
+#endif
+constexpr int kNormRowGroup = ZS_NORM_ROW_GROUP;  // rows loaded together (norm pass)
+#ifndef ZS_NORM_BLOCKS
+#define ZS_NORM_BLOCKS 16384
+#endif
+constexpr int kNormBlocks = ZS_NORM_BLOCKS;  // fixed grid of the norm pass
+#ifndef ZS_NORM_UNROLL
+#define ZS_NORM_UNROLL 4
+#endif
+constexpr int kNormUnroll = ZS_NORM_UNROLL;  // lane-vectors per lane per sweep
 #ifndef ZS_BLOCKS_PER_CU
-#define ZS_BLOCKS_PER_CU 8
+#define ZS_BLOCKS_PER_CU 0
+#endif
+#ifndef ZS_NT_STATE
+#define ZS_NT_STATE 0
+#endif
+#ifndef ZS_NT_SPILL
+#define ZS_NT_SPILL 0
 #endif
 
 struct Rows {
@@ -99,6 +116,18 @@ struct QuantArgs {
 };
 
 // ------------------------------------------------------------ device helpers
+
+template <bool NT, class T>
+__device__ __forceinline__ T ld(const T *p) {
+  if constexpr (NT) return __builtin_nontemporal_load(p);
+  else return *p;
+}
+
+template <bool NT, class T>
+__device__ __forceinline__ void st(T v, T *p) {
+  if constexpr (NT) __builtin_nontemporal_store(v, p);
+  else *p = v;
+}
 
 __device__ __forceinline__ float bf16_lo(unsigned w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(unsigned w) { return __uint_as_float(w & 0xffff0000u); }
@@ -229,17 +258,42 @@ __device__ __forceinline__ void quant_lane(const float (&p)[kVec], int nvalid, i
 
 // ------------------------------------------------------------------ kernels
 
-// a1 + a2 (apply) + a3 + a4 (+ a5 when QL > 0).  The loop runs over whole
-// waves so that every lane reaches the quantizer's shuffles together.
+// Averaged gradient of the U full lane-vectors v0, v0+64, .., v0+64(U-1)
+// (one per wave-sweep of 64 lanes): U*kRowGroup 16-byte loads in flight per
+// lane; per element the same k-ordered binary64 sum as reduce_average.
+template <int U, int G>
+__device__ __forceinline__ void reduce_average_wave(const Rows &rows, const Avg &avg, int64_t v0,
+                                                    float (&g)[U][kVec]) {
+  double s[U][kVec];
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+#pragma unroll
+    for (int e = 0; e < kVec; ++e) s[u][e] = 0.0;
+  for (int k0 = 0; k0 < avg.nd; k0 += G) {
+    u32x4 r[U][G];
+#pragma unroll
+    for (int j = 0; j < G; ++j)
+      if (k0 + j < avg.nd)
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+          r[u][j] = __builtin_nontemporal_load(rows.p[k0 + j] + v0 + 64 * u);
+#pragma unroll
+    for (int j = 0; j < G; ++j)
+      if (k0 + j < avg.nd)
+#pragma unroll
+        for (int u = 0; u < U; ++u) add_row(s[u], r[u][j]);
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+#pragma unroll
+    for (int e = 0; e < kVec; ++e) g[u][e] = average(s[u][e], avg);
+}
+
+// One lane-vector (8 elements) of the update, any fill level: nvalid = 0..8
+// valid elements.  Every lane of the wave calls it together (the quantizer
+// reduces across lanes); lanes past the end pass a vector with nvalid 0.
 template <int QL>
-__global__ void __launch_bounds__(kThreads) step_kernel(const StepArgs A) {
-  const int lane = threadIdx.x & 63;
-  const int64_t nvec = (A.n + kVec - 1) / kVec;
-  const int64_t stride = int64_t(gridDim.x) * kThreads;
-  const double coef = A.sumsq ? clip_coef(*A.sumsq, A.max_norm) : 1.0;
-  for (int64_t base = int64_t(blockIdx.x) * kThreads + (threadIdx.x & ~63); base < nvec;
-       base += stride) {
-    const int64_t vec = base + lane;
+__device__ __forceinline__ void step_vec(const StepArgs &A, int64_t vec, double coef) {
     const int64_t e0 = vec * kVec;
     const int nvalid = e0 + kVec <= A.n ? kVec : (e0 < A.n ? int(A.n - e0) : 0);
     float th[kVec], mo[kVec], va[kVec], g[kVec], p[kVec];
@@ -247,7 +301,9 @@ __global__ void __launch_bounds__(kThreads) step_kernel(const StepArgs A) {
       const f32x4 *t4 = reinterpret_cast<const f32x4 *>(A.master) + 2 * vec;
       const f32x4 *m4 = reinterpret_cast<const f32x4 *>(A.m) + 2 * vec;
       const f32x4 *v4 = reinterpret_cast<const f32x4 *>(A.v) + 2 * vec;
-      const f32x4 ta = t4[0], tb = t4[1], ma = m4[0], mb = m4[1], vx = v4[0], vy = v4[1];
+      constexpr bool nt = ZS_NT_STATE;
+      const f32x4 ta = ld<nt>(t4), tb = ld<nt>(t4 + 1), ma = ld<nt>(m4), mb = ld<nt>(m4 + 1),
+                  vx = ld<nt>(v4), vy = ld<nt>(v4 + 1);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         th[e] = ta[e]; th[e + 4] = tb[e];
@@ -300,9 +356,10 @@ __global__ void __launch_bounds__(kThreads) step_kernel(const StepArgs A) {
         o[2][e] = mo[e]; o[3][e] = mo[e + 4];
         o[4][e] = va[e]; o[5][e] = va[e + 4];
       }
-      t4[0] = o[0]; t4[1] = o[1];
-      m4[0] = o[2]; m4[1] = o[3];
-      v4[0] = o[4]; v4[1] = o[5];
+      constexpr bool nt = ZS_NT_STATE;
+      st<nt>(o[0], t4); st<nt>(o[1], t4 + 1);
+      st<nt>(o[2], m4); st<nt>(o[3], m4 + 1);
+      st<nt>(o[4], v4); st<nt>(o[5], v4 + 1);
       u32x4 pv;
       pv.x = pb[0]; pv.y = pb[1]; pv.z = pb[2]; pv.w = pb[3];
       __builtin_nontemporal_store(pv, reinterpret_cast<u32x4 *>(A.pout) + vec);
@@ -318,51 +375,171 @@ __global__ void __launch_bounds__(kThreads) step_kernel(const StepArgs A) {
       }
     }
     if constexpr (QL > 0) quant_lane<QL>(p, nvalid, vec, A.codes, A.scales);
+}
+
+#ifndef ZS_STEP_UNROLL
+#define ZS_STEP_UNROLL 1
+#endif
+constexpr int kStepUnroll = ZS_STEP_UNROLL;
+
+// a1 + a2 (apply) + a3 + a4 (+ a5 when QL > 0).  Each wave owns a chunk of
+// 64*U consecutive lane-vectors per iteration (lane l takes v0+l, v0+64+l,
+// ...), so every wave reads and writes U*1 KiB runs of each stream.  Full
+// chunks load all U vectors' state and contributions before computing; the
+// shard's last, partial chunk goes vector by vector.  The loop condition is
+// uniform across the wave, as the quantizer's shuffles need.
+template <int QL>
+__global__ void __launch_bounds__(kThreads) step_kernel(const StepArgs A) {
+  constexpr int U = kStepUnroll;
+  constexpr int64_t span = 64 * U;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int64_t nvec = (A.n + kVec - 1) / kVec;
+  const int64_t nfull = A.n / kVec;
+  const int64_t stride = int64_t(gridDim.x) * (kThreads / 64) * span;
+  const double coef = A.sumsq ? clip_coef(*A.sumsq, A.max_norm) : 1.0;
+  constexpr bool nt = ZS_NT_STATE;
+  for (int64_t wb = (int64_t(blockIdx.x) * (kThreads / 64) + wave) * span; wb < nvec;
+       wb += stride) {
+    if (U == 1 || wb + span > nfull) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) step_vec<QL>(A, wb + 64 * u + lane, coef);
+      continue;
+    }
+    float th[U][kVec], mo[U][kVec], va[U][kVec], g[U][kVec];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t vec = wb + 64 * u + lane;
+      const f32x4 *t4 = reinterpret_cast<const f32x4 *>(A.master) + 2 * vec;
+      const f32x4 *m4 = reinterpret_cast<const f32x4 *>(A.m) + 2 * vec;
+      const f32x4 *v4 = reinterpret_cast<const f32x4 *>(A.v) + 2 * vec;
+      const f32x4 ta = ld<nt>(t4), tb = ld<nt>(t4 + 1), ma = ld<nt>(m4), mb = ld<nt>(m4 + 1),
+                  vx = ld<nt>(v4), vy = ld<nt>(v4 + 1);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        th[u][e] = ta[e]; th[u][e + 4] = tb[e];
+        mo[u][e] = ma[e]; mo[u][e + 4] = mb[e];
+        va[u][e] = vx[e]; va[u][e + 4] = vy[e];
+      }
+    }
+    if (A.gbar) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const f32x4 *g4 = reinterpret_cast<const f32x4 *>(A.gbar) + 2 * (wb + 64 * u + lane);
+        const f32x4 ga = __builtin_nontemporal_load(g4), gb = __builtin_nontemporal_load(g4 + 1);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) { g[u][e] = ga[e]; g[u][e + 4] = gb[e]; }
+      }
+    } else {
+      reduce_average_wave<U, kRowGroup>(A.rows, A.avg, wb + lane, g);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t vec = wb + 64 * u + lane;
+#pragma unroll
+      for (int e = 0; e < kVec; ++e)
+        adam(coef * static_cast<double>(g[u][e]), th[u][e], mo[u][e], va[u][e], A.k);
+      unsigned pb[4];
+      float p[kVec];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        pb[e] = pack_bf16(th[u][2 * e], th[u][2 * e + 1]);
+        p[2 * e] = bf16_lo(pb[e]);
+        p[2 * e + 1] = bf16_hi(pb[e]);
+      }
+      f32x4 *t4 = reinterpret_cast<f32x4 *>(A.master) + 2 * vec;
+      f32x4 *m4 = reinterpret_cast<f32x4 *>(A.m) + 2 * vec;
+      f32x4 *v4 = reinterpret_cast<f32x4 *>(A.v) + 2 * vec;
+      f32x4 o[6];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        o[0][e] = th[u][e]; o[1][e] = th[u][e + 4];
+        o[2][e] = mo[u][e]; o[3][e] = mo[u][e + 4];
+        o[4][e] = va[u][e]; o[5][e] = va[u][e + 4];
+      }
+      st<nt>(o[0], t4); st<nt>(o[1], t4 + 1);
+      st<nt>(o[2], m4); st<nt>(o[3], m4 + 1);
+      st<nt>(o[4], v4); st<nt>(o[5], v4 + 1);
+      u32x4 pv;
+      pv.x = pb[0]; pv.y = pb[1]; pv.z = pb[2]; pv.w = pb[3];
+      __builtin_nontemporal_store(pv, reinterpret_cast<u32x4 *>(A.pout) + vec);
+      if constexpr (QL > 0) quant_lane<QL>(p, kVec, vec, A.codes, A.scales);
+    }
+  }
+}
+
+__device__ __forceinline__ void store_gbar(float *out, int64_t vec, int nvalid,
+                                           const float (&g)[kVec]) {
+  if (nvalid == kVec) {
+    f32x4 a, b;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) { a[e] = g[e]; b[e] = g[e + 4]; }
+    f32x4 *o = reinterpret_cast<f32x4 *>(out) + 2 * vec;
+    st<ZS_NT_SPILL>(a, o);
+    st<ZS_NT_SPILL>(b, o + 1);
+  } else {
+#pragma unroll
+    for (int e = 0; e < kVec; ++e)
+      if (e < nvalid) out[vec * kVec + e] = g[e];
   }
 }
 
 // a2, first kernel: block partial sums of gbar^2 (binary64).  The grid is
-// fixed by n alone; each block's partial is a fixed-order reduction.
+// fixed by n alone.  Each wave sweeps 64*kNormUnroll consecutive
+// lane-vectors per iteration (lane l takes v0+l, v0+64+l, ...); a lane's
+// sum runs over its vectors in sweep order, then a fixed butterfly over
+// the wave and the 4 wave sums in order.
 __global__ void __launch_bounds__(kThreads) gnorm_partial_kernel(const NormArgs A) {
+  constexpr int U = kNormUnroll;
+  constexpr int64_t span = 64 * U;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
   const int64_t nvec = (A.n + kVec - 1) / kVec;
-  const int64_t stride = int64_t(gridDim.x) * kThreads;
+  const int64_t nfull = A.n / kVec;
+  const int64_t stride = int64_t(gridDim.x) * (kThreads / 64) * span;
   double acc = 0.0;
-  for (int64_t vec = int64_t(blockIdx.x) * kThreads + threadIdx.x; vec < nvec; vec += stride) {
-    const int64_t e0 = vec * kVec;
-    const int nvalid = e0 + kVec <= A.n ? kVec : int(A.n - e0);
-    float g[kVec];
-    reduce_average(A.rows, A.avg, vec, nvalid, g);
-    if (A.gbar_out) {
-      if (nvalid == kVec) {
-        f32x4 a, b;
+  for (int64_t wb = (int64_t(blockIdx.x) * (kThreads / 64) + wave) * span; wb < nvec;
+       wb += stride) {
+    if (wb + span <= nfull) {
+      float g[U][kVec];
+      reduce_average_wave<U, kNormRowGroup>(A.rows, A.avg, wb + lane, g);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) { a[e] = g[e]; b[e] = g[e + 4]; }
-        f32x4 *o = reinterpret_cast<f32x4 *>(A.gbar_out) + 2 * vec;
-        o[0] = a;
-        o[1] = b;
-      } else {
+      for (int u = 0; u < U; ++u) {
+        if (A.gbar_out) store_gbar(A.gbar_out, wb + 64 * u + lane, kVec, g[u]);
 #pragma unroll
-        for (int e = 0; e < kVec; ++e)
-          if (e < nvalid) A.gbar_out[e0 + e] = g[e];
+        for (int e = 0; e < kVec; ++e) {
+          const double x = static_cast<double>(g[u][e]);
+          acc += x * x;
+        }
       }
-    }
+    } else {
+      for (int u = 0; u < U; ++u) {
+        const int64_t vec = wb + 64 * u + lane;
+        if (vec >= nvec) break;
+        const int64_t e0 = vec * kVec;
+        const int nvalid = e0 + kVec <= A.n ? kVec : int(A.n - e0);
+        float g[kVec];
+        reduce_average(A.rows, A.avg, vec, nvalid, g);
+        if (A.gbar_out) store_gbar(A.gbar_out, vec, nvalid, g);
 #pragma unroll
-    for (int e = 0; e < kVec; ++e) {
-      if (e < nvalid) {
-        const double x = static_cast<double>(g[e]);
-        acc += x * x;
+        for (int e = 0; e < kVec; ++e) {
+          if (e < nvalid) {
+            const double x = static_cast<double>(g[e]);
+            acc += x * x;
+          }
+        }
       }
     }
   }
   // wave: butterfly over 64 lanes; block: the 4 wave sums in wave order
   for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
   __shared__ double wsum[kThreads / 64];
-  if ((threadIdx.x & 63) == 0) wsum[threadIdx.x >> 6] = acc;
+  if (lane == 0) wsum[wave] = acc;
   __syncthreads();
   if (threadIdx.x == 0) {
-    double s = 0.0;
-    for (int w = 0; w < kThreads / 64; ++w) s += wsum[w];
-    A.partials[blockIdx.x] = s;
+    double t = 0.0;
+    for (int w = 0; w < kThreads / 64; ++w) t += wsum[w];
+    A.partials[blockIdx.x] = t;
   }
 }
 
@@ -446,8 +623,9 @@ int quant_lanes(int32_t block) {
   }
 }
 
-int64_t grid_blocks(const zs_handle *h, int64_t nvec) {
-  int64_t need = (nvec + kThreads - 1) / kThreads;
+int64_t grid_blocks(const zs_handle *h, int64_t nvec, int unroll) {
+  const int64_t per_block = int64_t(kThreads) * unroll;
+  int64_t need = (nvec + per_block - 1) / per_block;
   if (need < 1) need = 1;
   int64_t per_cu = ZS_BLOCKS_PER_CU;
   if (const char *e = std::getenv("ZS_BLOCKS_PER_CU")) per_cu = std::atoll(e);
@@ -574,7 +752,8 @@ int zero_shard_gnorm(zs_handle *h, const zs_bf16 *const *contrib, double *sumsq_
   if (rc) return rc;
   const hipStream_t st = static_cast<hipStream_t>(h->d.stream);
   const int64_t nvec = (n + kVec - 1) / kVec;
-  int64_t blocks = (nvec + kThreads - 1) / kThreads;
+  const int64_t per_block = int64_t(kThreads) * kNormUnroll;
+  int64_t blocks = (nvec + per_block - 1) / per_block;
   if (blocks > kNormBlocks) blocks = kNormBlocks;
   if (blocks < 1) blocks = 1;
   A.avg = make_avg(h->d.n_d);
@@ -634,7 +813,7 @@ int zero_shard_step(zs_handle *h, const zs_bf16 *const *contrib, float lr, int64
   A.scales = d.q_scales;
   const hipStream_t st = static_cast<hipStream_t>(d.stream);
   const int64_t nvec = (n + kVec - 1) / kVec;
-  const dim3 grid(unsigned(grid_blocks(h, nvec))), block(kThreads);
+  const dim3 grid(unsigned(grid_blocks(h, nvec, kStepUnroll))), block(kThreads);
   switch (d.quant_block) {
     case 0: hipLaunchKernelGGL(step_kernel<0>, grid, block, 0, st, A); break;
     case 32: hipLaunchKernelGGL(step_kernel<4>, grid, block, 0, st, A); break;
@@ -662,7 +841,7 @@ int zero_shard_quant(zs_handle *h, int32_t block) {
   QuantArgs A{d.param_out, n, d.q_codes, d.q_scales};
   const hipStream_t st = static_cast<hipStream_t>(d.stream);
   const int64_t nvec = (n + kVec - 1) / kVec;
-  const dim3 grid(unsigned(grid_blocks(h, nvec))), blk(kThreads);
+  const dim3 grid(unsigned(grid_blocks(h, nvec, 1))), blk(kThreads);
   switch (block) {
     case 32: hipLaunchKernelGGL(quant_kernel<4>, grid, blk, 0, st, A); break;
     case 64: hipLaunchKernelGGL(quant_kernel<8>, grid, blk, 0, st, A); break;

@@ -133,7 +133,7 @@ class OracleWindow:
         if self.w.max_norm > 0:
             assert sumsq_total is not None
             gbar = O.reduce_average(rows)
-            coef = O.clip_coef(sumsq_total, self.w.max_norm)
+            coef = O.clip_coef(sumsq_total, float(np.float32(self.w.max_norm)))
             O.adam(self.master, self.m, self.v, gbar, coef, h)
             p = O.f32_to_bf16(self.master)
             codes = scales = None

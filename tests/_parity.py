@@ -76,3 +76,17 @@ def int8_exact(name: str, gpu_codes: np.ndarray, gpu_scales: np.ndarray, orc_cod
         raise AssertionError(f"{name}: block {b} differs with identical input "
                              f"({int(bad_codes.sum())} code blocks, {int(bad_scales.sum())} scales)")
     return diff
+
+
+def sumsq_tolerance(n: int, s: float) -> float:
+    """Bound on |S_gpu - S_oracle| for two binary64 sums of the same n
+    non-negative (exact) squares in different orders: recursive summation of
+    m terms errs by at most (m-1) u S (u = 2^-53).  The oracle sums 2^20-
+    element chunks, then the chunk partials; the GPU sums per lane over a
+    fixed grid of at most 2048 x 256 lanes, then wave, block and partial
+    trees (< 64 levels)."""
+    u = 2.0 ** -53
+    chunk = 1 << 20
+    orc = min(n, chunk) + n // chunk + 1
+    gpu = n // (2048 * 256 * 8) + 8 + 64 + 2048
+    return (orc + gpu) * u * s

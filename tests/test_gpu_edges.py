@@ -56,7 +56,7 @@ def _run_pair(w: S.Workload, n: int, steps: int, *, bias_correction=True, spill=
         h = ow.hyper(s)
         if w.max_norm > 0:
             gbar, ssq = O.gbar_sumsq(list(rows_h))
-            coef = O.clip_coef(ssq, w.max_norm)
+            coef = O.clip_coef(ssq, float(np.float32(w.max_norm)))
             O.adam(ow.master, ow.m, ow.v, gbar, coef, h)
             p = O.f32_to_bf16(ow.master)
             codes = scales = None
