@@ -102,8 +102,8 @@ def measured_traffic(w, kernel: str) -> float | None:
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default=DEFAULT_WORKLOAD,
                     help="workload name or index (default: %(default)s)")
     ap.add_argument("--no-cpu-baseline", action="store_true")

@@ -377,20 +377,26 @@ __device__ __forceinline__ void step_vec(const StepArgs &A, int64_t vec, double 
     if constexpr (QL > 0) quant_lane<QL>(p, nvalid, vec, A.codes, A.scales);
 }
 
-#ifndef ZS_STEP_UNROLL
-#define ZS_STEP_UNROLL 1
+#ifndef ZS_WIDE_MIN_ROWS
+#define ZS_WIDE_MIN_ROWS 16
 #endif
-constexpr int kStepUnroll = ZS_STEP_UNROLL;
+#ifndef ZS_WIDE_ROW_GROUP
+#define ZS_WIDE_ROW_GROUP 4
+#endif
+constexpr int kWideMinRows = ZS_WIDE_MIN_ROWS;    // rows from which the update goes wide
+constexpr int kWideUnroll = 4;                    // lane-vectors per wave sweep when wide
+constexpr int kWideRowGroup = ZS_WIDE_ROW_GROUP;  // rows loaded together when wide
 
 // a1 + a2 (apply) + a3 + a4 (+ a5 when QL > 0).  Each wave owns a chunk of
 // 64*U consecutive lane-vectors per iteration (lane l takes v0+l, v0+64+l,
-// ...), so every wave reads and writes U*1 KiB runs of each stream.  Full
-// chunks load all U vectors' state and contributions before computing; the
+// ...).  U = 1: one vector per lane, state, gradient and outputs together.
+// U > 1 (many contribution rows): the rows of all U vectors are reduced
+// first, so that every wave reads U KiB runs of each row with U*G 16-byte
+// loads in flight, then each vector's state is updated in turn.  The
 // shard's last, partial chunk goes vector by vector.  The loop condition is
 // uniform across the wave, as the quantizer's shuffles need.
-template <int QL>
+template <int QL, int U>
 __global__ void __launch_bounds__(kThreads) step_kernel(const StepArgs A) {
-  constexpr int U = kStepUnroll;
   constexpr int64_t span = 64 * U;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -406,56 +412,39 @@ __global__ void __launch_bounds__(kThreads) step_kernel(const StepArgs A) {
       for (int u = 0; u < U; ++u) step_vec<QL>(A, wb + 64 * u + lane, coef);
       continue;
     }
-    float th[U][kVec], mo[U][kVec], va[U][kVec], g[U][kVec];
+    float g[U][kVec];
+    reduce_average_wave<U, kWideRowGroup>(A.rows, A.avg, wb + lane, g);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t vec = wb + 64 * u + lane;
-      const f32x4 *t4 = reinterpret_cast<const f32x4 *>(A.master) + 2 * vec;
-      const f32x4 *m4 = reinterpret_cast<const f32x4 *>(A.m) + 2 * vec;
-      const f32x4 *v4 = reinterpret_cast<const f32x4 *>(A.v) + 2 * vec;
-      const f32x4 ta = ld<nt>(t4), tb = ld<nt>(t4 + 1), ma = ld<nt>(m4), mb = ld<nt>(m4 + 1),
-                  vx = ld<nt>(v4), vy = ld<nt>(v4 + 1);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        th[u][e] = ta[e]; th[u][e + 4] = tb[e];
-        mo[u][e] = ma[e]; mo[u][e + 4] = mb[e];
-        va[u][e] = vx[e]; va[u][e + 4] = vy[e];
-      }
-    }
-    if (A.gbar) {
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const f32x4 *g4 = reinterpret_cast<const f32x4 *>(A.gbar) + 2 * (wb + 64 * u + lane);
-        const f32x4 ga = __builtin_nontemporal_load(g4), gb = __builtin_nontemporal_load(g4 + 1);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) { g[u][e] = ga[e]; g[u][e + 4] = gb[e]; }
-      }
-    } else {
-      reduce_average_wave<U, kRowGroup>(A.rows, A.avg, wb + lane, g);
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t vec = wb + 64 * u + lane;
-#pragma unroll
-      for (int e = 0; e < kVec; ++e)
-        adam(coef * static_cast<double>(g[u][e]), th[u][e], mo[u][e], va[u][e], A.k);
-      unsigned pb[4];
-      float p[kVec];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        pb[e] = pack_bf16(th[u][2 * e], th[u][2 * e + 1]);
-        p[2 * e] = bf16_lo(pb[e]);
-        p[2 * e + 1] = bf16_hi(pb[e]);
-      }
       f32x4 *t4 = reinterpret_cast<f32x4 *>(A.master) + 2 * vec;
       f32x4 *m4 = reinterpret_cast<f32x4 *>(A.m) + 2 * vec;
       f32x4 *v4 = reinterpret_cast<f32x4 *>(A.v) + 2 * vec;
+      const f32x4 ta = ld<nt>(t4), tb = ld<nt>(t4 + 1), ma = ld<nt>(m4), mb = ld<nt>(m4 + 1),
+                  vx = ld<nt>(v4), vy = ld<nt>(v4 + 1);
+      float th[kVec], mo[kVec], va[kVec], p[kVec];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        th[e] = ta[e]; th[e + 4] = tb[e];
+        mo[e] = ma[e]; mo[e + 4] = mb[e];
+        va[e] = vx[e]; va[e + 4] = vy[e];
+      }
+#pragma unroll
+      for (int e = 0; e < kVec; ++e)
+        adam(coef * static_cast<double>(g[u][e]), th[e], mo[e], va[e], A.k);
+      unsigned pb[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        pb[e] = pack_bf16(th[2 * e], th[2 * e + 1]);
+        p[2 * e] = bf16_lo(pb[e]);
+        p[2 * e + 1] = bf16_hi(pb[e]);
+      }
       f32x4 o[6];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        o[0][e] = th[u][e]; o[1][e] = th[u][e + 4];
-        o[2][e] = mo[u][e]; o[3][e] = mo[u][e + 4];
-        o[4][e] = va[u][e]; o[5][e] = va[u][e + 4];
+        o[0][e] = th[e]; o[1][e] = th[e + 4];
+        o[2][e] = mo[e]; o[3][e] = mo[e + 4];
+        o[4][e] = va[e]; o[5][e] = va[e + 4];
       }
       st<nt>(o[0], t4); st<nt>(o[1], t4 + 1);
       st<nt>(o[2], m4); st<nt>(o[3], m4 + 1);
@@ -543,15 +532,18 @@ __global__ void __launch_bounds__(kThreads) gnorm_partial_kernel(const NormArgs 
   }
 }
 
-// a2, second kernel: one block reduces the partials in a fixed order.
-__global__ void __launch_bounds__(kThreads) gnorm_final_kernel(const double *partials, int np,
-                                                               double *out) {
-  __shared__ double buf[kThreads];
+// a2, second kernel: one block of 1024 reduces the partials in a fixed
+// order (each thread a strided run, then an LDS tree).
+constexpr int kFinalThreads = 1024;
+
+__global__ void __launch_bounds__(kFinalThreads) gnorm_final_kernel(const double *partials,
+                                                                    int np, double *out) {
+  __shared__ double buf[kFinalThreads];
   double s = 0.0;
-  for (int i = threadIdx.x; i < np; i += kThreads) s += partials[i];
+  for (int i = threadIdx.x; i < np; i += kFinalThreads) s += partials[i];
   buf[threadIdx.x] = s;
   __syncthreads();
-  for (int half = kThreads / 2; half >= 1; half >>= 1) {
+  for (int half = kFinalThreads / 2; half >= 1; half >>= 1) {
     if (threadIdx.x < half) buf[threadIdx.x] += buf[threadIdx.x + half];
     __syncthreads();
   }
@@ -762,7 +754,7 @@ int zero_shard_gnorm(zs_handle *h, const zs_bf16 *const *contrib, double *sumsq_
   A.partials = h->partials;
   hipLaunchKernelGGL(gnorm_partial_kernel, dim3(unsigned(blocks)), dim3(kThreads), 0, st, A);
   if ((rc = launched())) return rc;
-  hipLaunchKernelGGL(gnorm_final_kernel, dim3(1), dim3(kThreads), 0, st,
+  hipLaunchKernelGGL(gnorm_final_kernel, dim3(1), dim3(kFinalThreads), 0, st,
                      static_cast<const double *>(h->partials), int(blocks), sumsq_dev);
   if ((rc = launched())) return rc;
   h->spill_valid = h->d.gbar_ws != nullptr;
@@ -813,16 +805,25 @@ int zero_shard_step(zs_handle *h, const zs_bf16 *const *contrib, float lr, int64
   A.scales = d.q_scales;
   const hipStream_t st = static_cast<hipStream_t>(d.stream);
   const int64_t nvec = (n + kVec - 1) / kVec;
-  const dim3 grid(unsigned(grid_blocks(h, nvec, kStepUnroll))), block(kThreads);
+  const bool wide = !A.gbar && d.n_d >= kWideMinRows;
+  const dim3 grid(unsigned(grid_blocks(h, nvec, wide ? kWideUnroll : 1))), block(kThreads);
+#define ZS_LAUNCH_STEP(QL)                                                           \
+  do {                                                                               \
+    if (wide)                                                                        \
+      hipLaunchKernelGGL((step_kernel<QL, kWideUnroll>), grid, block, 0, st, A);     \
+    else                                                                             \
+      hipLaunchKernelGGL((step_kernel<QL, 1>), grid, block, 0, st, A);               \
+  } while (0)
   switch (d.quant_block) {
-    case 0: hipLaunchKernelGGL(step_kernel<0>, grid, block, 0, st, A); break;
-    case 32: hipLaunchKernelGGL(step_kernel<4>, grid, block, 0, st, A); break;
-    case 64: hipLaunchKernelGGL(step_kernel<8>, grid, block, 0, st, A); break;
-    case 128: hipLaunchKernelGGL(step_kernel<16>, grid, block, 0, st, A); break;
-    case 256: hipLaunchKernelGGL(step_kernel<32>, grid, block, 0, st, A); break;
-    case 512: hipLaunchKernelGGL(step_kernel<64>, grid, block, 0, st, A); break;
+    case 0: ZS_LAUNCH_STEP(0); break;
+    case 32: ZS_LAUNCH_STEP(4); break;
+    case 64: ZS_LAUNCH_STEP(8); break;
+    case 128: ZS_LAUNCH_STEP(16); break;
+    case 256: ZS_LAUNCH_STEP(32); break;
+    case 512: ZS_LAUNCH_STEP(64); break;
     default: return ZS_EINVAL;
   }
+#undef ZS_LAUNCH_STEP
   return launched();
 }
 

@@ -93,6 +93,8 @@ CASES = [
     ("gpt2-small-flat", 65536 + 13, 8, 128, 0.0),
     ("13B-nd16-clip-int8", 300_001, 16, 256, 1.0),
     ("7.5B-nd64", 20_000 + 4, 64, 0, 0.0),
+    ("gpt2-small-flat", 100_003, 32, 256, 0.0),
+    ("13B-nd16-clip-int8", 70_000 + 1, 16, 64, 0.0),
 ]
 
 
