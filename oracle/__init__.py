@@ -98,6 +98,14 @@ def lib() -> ctypes.CDLL:
                                ctypes.POINTER(OrcHyper), ctypes.POINTER(_c_f64), _c_i32]
         L.orc_gbar_sumsq.restype = _c_f64
         L.orc_gbar_sumsq.argtypes = [_vp, _c_i32, _c_i64, _vp, _c_i32]
+        L.orc_reduce_sum_q8.argtypes = [_vp, _vp, _c_i32, _c_i64, _c_i32, _vp]
+        L.orc_reduce_average_q8.argtypes = [_vp, _vp, _c_i32, _c_i64, _c_i32, _vp]
+        L.orc_gbar_sumsq_q8.restype = _c_f64
+        L.orc_gbar_sumsq_q8.argtypes = [_vp, _vp, _c_i32, _c_i64, _c_i32, _vp, _c_i32]
+        L.orc_step_q8.restype = ctypes.c_int
+        L.orc_step_q8.argtypes = [_vp, _vp, _c_i32, _c_i64, _c_i32, _vp, _vp, _vp, _vp, _vp,
+                                  _vp, ctypes.POINTER(OrcHyper), ctypes.POINTER(_c_f64),
+                                  _c_i32]
         _lib = L
     return _lib
 
@@ -114,6 +122,19 @@ def _rows(rows) -> tuple[ctypes.Array, int, int]:
     arr = (ctypes.c_void_p * len(rows))(*[_ptr(r) for r in rows])
     arr._keep = rows  # keep the arrays alive with the pointer table
     return arr, len(rows), n
+
+
+def _q8(codes, scales, block: int):
+    codes = [np.ascontiguousarray(c, dtype=np.int8) for c in codes]
+    n = codes[0].size if codes else 0
+    nb = (n + block - 1) // block
+    scales = [np.ascontiguousarray(x, dtype=np.float32) for x in scales]
+    assert len(codes) == len(scales) and all(c.size == n for c in codes)
+    assert all(x.size >= nb for x in scales)
+    ct = (ctypes.c_void_p * len(codes))(*[_ptr(c) for c in codes])
+    st = (ctypes.c_void_p * len(scales))(*[_ptr(x) for x in scales])
+    ct._keep, st._keep = codes, scales
+    return ct, st, len(codes), n
 
 
 def model_state_bytes(n_params: float, n_gpus: float, stage: int, k: float = 12.0) -> float:
@@ -145,6 +166,27 @@ def reduce_average(rows) -> np.ndarray:
     out = np.empty(n, dtype=np.float32)
     lib().orc_reduce_average(arr, nd, n, _ptr(out))
     return out
+
+
+def reduce_sum_q8(codes, scales, block: int) -> np.ndarray:
+    ct, st, nd, n = _q8(codes, scales, block)
+    out = np.empty(n, dtype=np.float64)
+    lib().orc_reduce_sum_q8(ct, st, nd, n, int(block), _ptr(out))
+    return out
+
+
+def reduce_average_q8(codes, scales, block: int) -> np.ndarray:
+    ct, st, nd, n = _q8(codes, scales, block)
+    out = np.empty(n, dtype=np.float32)
+    lib().orc_reduce_average_q8(ct, st, nd, n, int(block), _ptr(out))
+    return out
+
+
+def gbar_sumsq_q8(codes, scales, block: int, threads: int = 1) -> tuple[np.ndarray, float]:
+    ct, st, nd, n = _q8(codes, scales, block)
+    g = np.empty(n, dtype=np.float32)
+    s = lib().orc_gbar_sumsq_q8(ct, st, nd, n, int(block), _ptr(g), int(threads))
+    return g, s
 
 
 def sumsq(gbar: np.ndarray) -> float:
@@ -211,3 +253,26 @@ def step(rows, master: np.ndarray, m: np.ndarray, v: np.ndarray, h: Hyper,
     if rc != 0:
         raise ValueError(f"orc_step rejected its arguments (rc={rc})")
     return StepOut(p, codes, scales, s.value)
+
+
+def step_q8(codes, scales, block: int, master: np.ndarray, m: np.ndarray, v: np.ndarray,
+            h: Hyper, threads: int = 1) -> StepOut:
+    """One shard step with int8 contributions (value = code * scale of its
+    block).  master, m, v are updated in place."""
+    ct, st, nd, n = _q8(codes, scales, block)
+    for a in (master, m, v):
+        assert a.dtype == np.float32 and a.flags["C_CONTIGUOUS"] and a.size == n
+    p = np.empty(n, dtype=np.uint16)
+    qc = qs = None
+    cp = sp = None
+    if h.quant_block > 0:
+        qc = np.empty(n, dtype=np.int8)
+        qs = np.empty((n + h.quant_block - 1) // h.quant_block, dtype=np.float32)
+        cp, sp = _ptr(qc), _ptr(qs)
+    s = _c_f64(0.0)
+    hc = h.to_c()
+    rc = lib().orc_step_q8(ct, st, nd, n, int(block), _ptr(master), _ptr(m), _ptr(v), _ptr(p),
+                           cp, sp, ctypes.byref(hc), ctypes.byref(s), int(threads))
+    if rc != 0:
+        raise ValueError(f"orc_step_q8 rejected its arguments (rc={rc})")
+    return StepOut(p, qc, qs, s.value)

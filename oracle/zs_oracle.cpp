@@ -118,6 +118,33 @@ void orc_reduce_average(const uint16_t *const *rows, int32_t nd, int64_t n,
   }
 }
 
+/* a1 with quantized contributions.  ZeRO++ qgZ ("ZeRO (딥 러닝)", follow-ups
+ * table "후속 기법") sends each rank's gradient as quantized blocks that are
+ * averaged after the all-to-all.  The pages give no format; reading: int8
+ * codes with one binary32 scale per block of `block` shard elements, value
+ * = code * scale.  Each product is exact in binary64 (8 + 24 bits); the
+ * products are summed in rank order and the mean is rounded once to
+ * binary32, exactly as for bf16 contributions. */
+void orc_reduce_sum_q8(const int8_t *const *codes, const float *const *scales, int32_t nd,
+                       int64_t n, int32_t block, double *sums) {
+  for (int64_t i = 0; i < n; ++i) {
+    double s = 0.0;
+    for (int32_t k = 0; k < nd; ++k)
+      s += double(codes[k][i]) * double(scales[k][i / block]);
+    sums[i] = s;
+  }
+}
+
+void orc_reduce_average_q8(const int8_t *const *codes, const float *const *scales,
+                           int32_t nd, int64_t n, int32_t block, float *gbar) {
+  for (int64_t i = 0; i < n; ++i) {
+    double s = 0.0;
+    for (int32_t k = 0; k < nd; ++k)
+      s += double(codes[k][i]) * double(scales[k][i / block]);
+    gbar[i] = float(s / double(nd));
+  }
+}
+
 /* a2.  Global-norm clipping at gradient_clipping = 1.0 (WIKI "DeepSpeed에서
  * 쓰기").  The pages give no formula; reading: the L2 norm of the averaged
  * gradient, coef = min(1, max_norm / (norm + 1e-6)).  Each square of a
@@ -227,6 +254,54 @@ double orc_gbar_sumsq(const uint16_t *const *rows, int32_t nd, int64_t n,
   return s;
 }
 
+double orc_gbar_sumsq_q8(const int8_t *const *codes, const float *const *scales, int32_t nd,
+                         int64_t n, int32_t block, float *gbar, int32_t threads) {
+  const int64_t nchunks = (n + kChunk - 1) / kChunk;
+  std::vector<double> part(size_t(nchunks > 0 ? nchunks : 1), 0.0);
+  for_chunks(n, threads, [&](int64_t c) {
+    const int64_t lo = c * kChunk;
+    const int64_t len = lo + kChunk < n ? kChunk : n - lo;
+    std::vector<const int8_t *> cr(static_cast<size_t>(nd), nullptr);
+    std::vector<const float *> sr(static_cast<size_t>(nd), nullptr);
+    for (int32_t k = 0; k < nd; ++k) {
+      cr[size_t(k)] = codes[k] + lo;
+      sr[size_t(k)] = scales[k] + lo / block;
+    }
+    orc_reduce_average_q8(cr.data(), sr.data(), nd, len, block, gbar + lo);
+    part[size_t(c)] = orc_sumsq(gbar + lo, len);
+  });
+  double s = 0.0;
+  for (int64_t c = 0; c < nchunks; ++c) s += part[size_t(c)];
+  return s;
+}
+
+namespace {
+
+/* a2 (apply) .. a5 from the averaged gradient of the whole shard. */
+int finish_step(const float *gbar, double p, int64_t n, float *master, float *m, float *v,
+                uint16_t *p_out, int8_t *codes, float *scales, const orc_hyper *h,
+                double *sumsq_out, int32_t threads) {
+  double coef = 1.0;
+  if (h->max_norm > 0.0) coef = orc_clip_coef(p + h->s_other, h->max_norm);
+  if (sumsq_out) *sumsq_out = p;
+  for_chunks(n, threads, [&](int64_t c) {
+    const int64_t lo = c * kChunk;
+    const int64_t len = lo + kChunk < n ? kChunk : n - lo;
+    orc_adam(master + lo, m + lo, v + lo, gbar + lo, coef, len, h);
+    orc_cast_bf16(master + lo, len, p_out + lo);
+  });
+  if (h->quant_block > 0) orc_quant_int8(p_out, n, h->quant_block, codes, scales);
+  return 0;
+}
+
+bool bad_args(int32_t nd, int64_t n, const orc_hyper *h, const int8_t *codes,
+              const float *scales) {
+  if (nd < 1 || n < 0 || !h || h->t < 1) return true;
+  return h->quant_block < 0 || (h->quant_block > 0 && (!codes || !scales));
+}
+
+}  // namespace
+
 /* The shard step in the order the pages give it: the slice owner reduces
  * and averages its slice, updates its own fp32 states with it, and emits the
  * half-precision copy that the all-gather distributes (BIMU
@@ -237,9 +312,7 @@ double orc_gbar_sumsq(const uint16_t *const *rows, int32_t nd, int64_t n,
 int orc_step(const uint16_t *const *rows, int32_t nd, int64_t n, float *master,
              float *m, float *v, uint16_t *p_out, int8_t *codes, float *scales,
              const orc_hyper *h, double *sumsq_out, int32_t threads) {
-  if (nd < 1 || n < 0 || !h || h->t < 1) return -1;
-  if (h->quant_block < 0 || (h->quant_block > 0 && (!codes || !scales)))
-    return -1;
+  if (bad_args(nd, n, h, codes, scales)) return -1;
   if (n == 0) {
     if (sumsq_out) *sumsq_out = 0.0;
     return 0;
@@ -247,22 +320,28 @@ int orc_step(const uint16_t *const *rows, int32_t nd, int64_t n, float *master,
   float *gbar = static_cast<float *>(std::malloc(size_t(n) * sizeof(float)));
   if (!gbar) return -1;
   const double p = orc_gbar_sumsq(rows, nd, n, gbar, threads);
-  double coef = 1.0;
-  if (h->max_norm > 0.0) {
-    coef = orc_clip_coef(p + h->s_other, h->max_norm);
-    if (sumsq_out) *sumsq_out = p;
-  } else if (sumsq_out) {
-    *sumsq_out = p;
-  }
-  for_chunks(n, threads, [&](int64_t c) {
-    const int64_t lo = c * kChunk;
-    const int64_t len = lo + kChunk < n ? kChunk : n - lo;
-    orc_adam(master + lo, m + lo, v + lo, gbar + lo, coef, len, h);
-    orc_cast_bf16(master + lo, len, p_out + lo);
-  });
+  const int rc = finish_step(gbar, p, n, master, m, v, p_out, codes, scales, h, sumsq_out,
+                             threads);
   std::free(gbar);
-  if (h->quant_block > 0) orc_quant_int8(p_out, n, h->quant_block, codes, scales);
-  return 0;
+  return rc;
+}
+
+int orc_step_q8(const int8_t *const *qc, const float *const *qs, int32_t nd, int64_t n,
+                int32_t block, float *master, float *m, float *v, uint16_t *p_out,
+                int8_t *codes, float *scales, const orc_hyper *h, double *sumsq_out,
+                int32_t threads) {
+  if (bad_args(nd, n, h, codes, scales) || block < 1 || kChunk % block != 0) return -1;
+  if (n == 0) {
+    if (sumsq_out) *sumsq_out = 0.0;
+    return 0;
+  }
+  float *gbar = static_cast<float *>(std::malloc(size_t(n) * sizeof(float)));
+  if (!gbar) return -1;
+  const double p = orc_gbar_sumsq_q8(qc, qs, nd, n, block, gbar, threads);
+  const int rc = finish_step(gbar, p, n, master, m, v, p_out, codes, scales, h, sumsq_out,
+                             threads);
+  std::free(gbar);
+  return rc;
 }
 
 }  // extern "C"

@@ -58,6 +58,15 @@ void orc_reduce_sum(const uint16_t *const *rows, int32_t n_d, int64_t n,
 void orc_reduce_average(const uint16_t *const *rows, int32_t n_d, int64_t n,
                         float *gbar);
 
+/* a1 with int8 contributions (ZeRO++ qgZ): row k is codes[k] (int8) with
+ * one fp32 scale per `block` elements, scales[k][i / block]; element i of
+ * row k stands for code * scale.  Same rank-order binary64 sum, same single
+ * rounding of the average. */
+void orc_reduce_sum_q8(const int8_t *const *codes, const float *const *scales, int32_t n_d,
+                       int64_t n, int32_t block, double *sums);
+void orc_reduce_average_q8(const int8_t *const *codes, const float *const *scales,
+                           int32_t n_d, int64_t n, int32_t block, float *gbar);
+
 /* a2: sum of squares of gbar (fp64, index order). */
 double orc_sumsq(const float *gbar, int64_t n);
 double orc_clip_coef(double sumsq, double max_norm);
@@ -84,6 +93,16 @@ int orc_step(const uint16_t *const *rows, int32_t n_d, int64_t n,
  * same way (for callers that stream a large shard through in pieces). */
 double orc_gbar_sumsq(const uint16_t *const *rows, int32_t n_d, int64_t n,
                       float *gbar, int32_t threads);
+double orc_gbar_sumsq_q8(const int8_t *const *codes, const float *const *scales, int32_t n_d,
+                         int64_t n, int32_t block, float *gbar, int32_t threads);
+
+/* The whole step with int8 contributions (qgZ front end, then a2..a5 as in
+ * orc_step).  `block` must divide 2^20 (the chunk) so that blocks never
+ * straddle chunks. */
+int orc_step_q8(const int8_t *const *codes, const float *const *scales, int32_t n_d,
+                int64_t n, int32_t block, float *master, float *m, float *v,
+                uint16_t *p_out, int8_t *q_codes, float *q_scales, const orc_hyper *h,
+                double *sumsq_out, int32_t threads);
 
 #ifdef __cplusplus
 }

@@ -20,7 +20,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 HOST_LIB = os.path.join(_HERE, "libzsgen_host.so")
 DEV_LIB = os.path.join(_HERE, "libzsgen_dev.so")
 
-MASTER, MOM, VAR, GRAD, AUX = 0, 1, 2, 3, 4
+MASTER, MOM, VAR, GRAD, AUX, GRAD_SCALE = 0, 1, 2, 3, 4, 5
 KIND_NORMAL, KIND_ABS = 0, 1
 
 _u64, _u32, _i64, _i32, _f32, _vp = (ctypes.c_uint64, ctypes.c_uint32, ctypes.c_int64,
@@ -44,6 +44,8 @@ def host_lib() -> ctypes.CDLL:
                                          ctypes.c_int, ctypes.c_int]
         L.zsg_host_fill_contrib.argtypes = [_vp, _i32, _i64, _i64, _u64, _u32, _i64, _f32,
                                             ctypes.c_int, ctypes.c_int]
+        L.zsg_host_fill_contrib_q8.argtypes = [_vp, _vp, _i32, _i64, _i64, _i64, _u64, _u32,
+                                               _i64, _i32, _f32, ctypes.c_int]
         _host = L
     return _host
 
@@ -65,6 +67,9 @@ def dev_lib() -> ctypes.CDLL:
         L.zsg_dev_fill_contrib.restype = ctypes.c_int
         L.zsg_dev_fill_contrib.argtypes = [_vp, _i32, _i64, _i64, _u64, _u32, _i64, _f32,
                                            ctypes.c_int, _vp]
+        L.zsg_dev_fill_contrib_q8.restype = ctypes.c_int
+        L.zsg_dev_fill_contrib_q8.argtypes = [_vp, _vp, _i32, _i64, _i64, _i64, _u64, _u32,
+                                              _i64, _i32, _f32, _vp]
         _dev = L
     return _dev
 
@@ -106,6 +111,21 @@ def host_contrib(w: Workload, step: int, i0: int, n: int) -> np.ndarray:
     host_lib().zsg_host_fill_contrib(out.ctypes.data, w.n_d, int(n), int(n), w.seed, int(step),
                                      int(i0), float(w.grad_sigma), int(w.outliers), _threads())
     return out
+
+
+def host_contrib_q8(w: Workload, step: int, i0: int, n: int) -> tuple[np.ndarray, np.ndarray]:
+    """Int8 contributions of every rank for shard elements [i0, i0+n) at
+    step `step`: codes [n_d, n] and the scales [n_d, nb] of the blocks those
+    elements fall in (i0 a multiple of the block)."""
+    blk = w.contrib_block
+    assert blk > 0 and i0 % blk == 0
+    nb = (int(n) + blk - 1) // blk
+    codes = np.empty((w.n_d, int(n)), dtype=np.int8)
+    scales = np.empty((w.n_d, max(1, nb)), dtype=np.float32)
+    host_lib().zsg_host_fill_contrib_q8(codes.ctypes.data, scales.ctypes.data, w.n_d, int(n),
+                                        scales.shape[1], int(n), w.seed, int(step), int(i0),
+                                        blk, float(w.scale_sigma), _threads())
+    return codes, scales[:, :nb]
 
 
 def host_state(w: Workload, i0: int, n: int) -> tuple[np.ndarray, np.ndarray, np.ndarray]:
@@ -163,6 +183,18 @@ def dev_contrib(w: Workload, step: int, buf, n: int, row_stride: int, i0: int = 
                                           w.seed, int(step), int(i0), float(w.grad_sigma),
                                           int(w.outliers), _stream(stream)),
            "zsg_dev_fill_contrib")
+
+
+def dev_contrib_q8(w: Workload, step: int, codes, scales, n: int, code_stride: int,
+                   scale_stride: int, i0: int = 0, stream=None) -> None:
+    """Fill rank k's int8 codes at codes[k*code_stride:] and its block scales
+    at scales[k*scale_stride:] for shard elements [i0, i0+n)."""
+    assert codes.is_cuda and codes.element_size() == 1 and scales.is_cuda
+    _check(dev_lib().zsg_dev_fill_contrib_q8(codes.data_ptr(), scales.data_ptr(), w.n_d,
+                                             int(code_stride), int(scale_stride), int(n),
+                                             w.seed, int(step), int(i0), w.contrib_block,
+                                             float(w.scale_sigma), _stream(stream)),
+           "zsg_dev_fill_contrib_q8")
 
 
 def dev_state(w: Workload, master, m, v, i0: int = 0, stream=None) -> None:

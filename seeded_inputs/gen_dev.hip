@@ -25,6 +25,13 @@ fill_bf16(uint16_t *out, int64_t n, uint64_t h, int64_t i0, float sigma, int out
     out[j] = zsg_to_bf16(zsg_value(h, uint64_t(i0 + j), sigma, outliers, ZSG_KIND_NORMAL));
 }
 
+__global__ void __launch_bounds__(kThreads)
+fill_code(int8_t *out, int64_t n, uint64_t h, int64_t i0) {
+  const int64_t stride = int64_t(gridDim.x) * kThreads;
+  for (int64_t j = int64_t(blockIdx.x) * kThreads + threadIdx.x; j < n; j += stride)
+    out[j] = zsg_code(h, uint64_t(i0 + j));
+}
+
 unsigned grid_for(int64_t n) {
   int64_t b = (n + kThreads - 1) / kThreads;
   if (b > 65536) b = 65536;
@@ -66,6 +73,28 @@ int zsg_dev_fill_contrib(void *out, int32_t n_d, int64_t row_stride, int64_t n,
     const int rc = zsg_dev_fill_bf16(static_cast<uint16_t *>(out) + k * row_stride, n, seed,
                                      ZSG_GRAD, step, uint32_t(k), i0, sigma, outliers, stream);
     if (rc) return rc;
+  }
+  return 0;
+}
+
+/* Int8 contributions of one step (see the host build): rank k's codes at
+ * codes + k*code_stride, its block scales at scales + k*scale_stride. */
+int zsg_dev_fill_contrib_q8(void *codes, void *scales, int32_t n_d, int64_t code_stride,
+                            int64_t scale_stride, int64_t n, uint64_t seed, uint32_t step,
+                            int64_t i0, int32_t block, float scale_sigma, void *stream) {
+  if (n <= 0) return 0;
+  if (!codes || !scales || block < 1 || i0 % block) return -1;
+  const int64_t b0 = i0 / block;
+  const int64_t nb = (i0 + n - 1) / block - b0 + 1;
+  for (int32_t k = 0; k < n_d; ++k) {
+    const uint64_t hc = zsg_key(seed, ZSG_GRAD, step, uint32_t(k));
+    const uint64_t hs = zsg_key(seed, ZSG_GRAD_SCALE, step, uint32_t(k));
+    hipLaunchKernelGGL(fill_code, dim3(grid_for(n)), dim3(kThreads), 0, hipStream_t(stream),
+                       static_cast<int8_t *>(codes) + k * code_stride, n, hc, i0);
+    hipLaunchKernelGGL(fill_f32, dim3(grid_for(nb)), dim3(kThreads), 0, hipStream_t(stream),
+                       static_cast<float *>(scales) + k * scale_stride, nb, hs, b0, scale_sigma,
+                       0, int(ZSG_KIND_ABS));
+    if (hipGetLastError() != hipSuccess) return -4;
   }
   return 0;
 }

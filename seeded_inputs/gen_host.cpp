@@ -83,4 +83,31 @@ void zsg_host_fill_contrib(uint16_t *out, int32_t n_d, int64_t row_stride,
                        outliers, threads);
 }
 
+/* Int8 contributions of one step: codes of rank k at codes + k*code_stride
+ * (elements [i0, i0+n) of the shard), and the scales of the blocks those
+ * elements fall in, blocks [i0/block, (i0+n-1)/block], at scales +
+ * k*scale_stride.  i0 must be a multiple of block. */
+void zsg_host_fill_contrib_q8(int8_t *codes, float *scales, int32_t n_d, int64_t code_stride,
+                              int64_t scale_stride, int64_t n, uint64_t seed, uint32_t step,
+                              int64_t i0, int32_t block, float scale_sigma, int threads) {
+  const int64_t b0 = i0 / block;
+  const int64_t nb = n > 0 ? (i0 + n - 1) / block - b0 + 1 : 0;
+  if (threads < 1) threads = 1;
+  const int t = threads < n_d ? threads : n_d;
+  std::vector<std::thread> pool;
+  for (int w = 0; w < t; ++w)
+    pool.emplace_back([=] {
+      for (int32_t k = w; k < n_d; k += t) {
+        const uint64_t hc = zsg_key(seed, ZSG_GRAD, step, uint32_t(k));
+        const uint64_t hs = zsg_key(seed, ZSG_GRAD_SCALE, step, uint32_t(k));
+        int8_t *c = codes + k * code_stride;
+        float *sc = scales + k * scale_stride;
+        for (int64_t j = 0; j < n; ++j) c[j] = zsg_code(hc, uint64_t(i0 + j));
+        for (int64_t b = 0; b < nb; ++b)
+          sc[b] = zsg_value(hs, uint64_t(b0 + b), scale_sigma, 0, ZSG_KIND_ABS);
+      }
+    });
+  for (auto &th : pool) th.join();
+}
+
 }  // extern "C"

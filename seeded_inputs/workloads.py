@@ -50,12 +50,21 @@ class Workload:
     weight_decay: float = 0.0
     max_norm: float = 0.0    # > 0: global-norm clipping
     quant_block: int = 0     # > 0: int8 block quantization of the bf16 shard
+    contrib_block: int = 0   # > 0: contributions arrive as int8 codes with one
+                             # fp32 scale per contrib_block elements (qgZ)
     t0: int = 0              # step counter before the first step
     segments: tuple = field(default=(), compare=False)
 
     @property
     def seed(self) -> int:
         return SEED_BASE + self.index
+
+    @property
+    def scale_sigma(self) -> float:
+        """sigma of the |N(0, sigma)| per-block scales of int8 contributions:
+        codes have standard deviation 32, so code * scale has about the
+        gradient's sigma."""
+        return self.grad_sigma / 32.0
 
     @property
     def shard_len(self) -> int:
@@ -69,18 +78,21 @@ class Workload:
 
     def bytes_per_param(self, spill: bool = True) -> float:
         """Algorithmic HBM bytes per parameter of one whole step: N_d bf16
-        contributions, fp32 master/m/v read and written, the bf16 output;
+        contributions (or int8 codes plus a scale per block), fp32 master/m/v read and written, the bf16 output;
         with clipping the averaged gradient is spilled once as fp32 (written
         by the norm pass, read by the update), or the contributions are read
         twice; int8 codes plus one fp32 scale per block."""
-        b = 2.0 * self.n_d + 24.0 + 2.0
+        row = (1.0 + 4.0 / self.contrib_block) if self.contrib_block else 2.0
+        b = row * self.n_d + 24.0 + 2.0
         if self.max_norm > 0:
-            b += 8.0 if spill else 2.0 * self.n_d
+            b += 8.0 if spill else row * self.n_d
         if self.quant_block:
             b += 1.0 + 4.0 / self.quant_block
         return b
 
 
+# 0-4: the five shard-step workloads; 5: the 7.5B one with ZeRO++'s
+# quantized gradients in (qgZ) and quantized weights out (qwZ).
 WORKLOADS = [
     Workload(0, "tiny-zero1", phi=1_048_576, n_d=4, r=0, steps=10, grad_sigma=1e-3),
     Workload(1, "gpt2-small-flat", phi=124_439_808, n_d=8, r=0, steps=100,
@@ -91,6 +103,9 @@ WORKLOADS = [
              grad_sigma=1e-3, lr=1e-4, weight_decay=0.1, max_norm=1.0, quant_block=256),
     Workload(4, "13B-nd1-stage0", phi=sum(s for _, s in _seg13b()), n_d=1, r=0, steps=20,
              grad_sigma=1e-3, segments=tuple(_seg13b())),
+    Workload(5, "7.5B-nd64-zeropp", phi=7_500_000_000, n_d=64, r=0, steps=50,
+             grad_sigma=5e-4, warm=True, m_sigma=1e-4, v_sigma=1e-6, lr=1e-4, beta2=0.95,
+             t0=1000, quant_block=256, contrib_block=256),
 ]
 
 

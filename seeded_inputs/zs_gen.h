@@ -17,7 +17,9 @@
  *   z = (sum_fields - 12 * 32767.5) * 2^-16      (exact in binary32)
  * which has mean 0, variance 1 and support [-6, 6].  A draw of N(0, sigma)
  * is x = fl32(sigma * z); with outliers on, x = fl32(100 * x) when
- * (w_3 >> 32) mod 100 == 0, i.e. for 1% of the elements.  Only integer
+ * (w_3 >> 32) mod 100 == 0, i.e. for 1% of the elements.  Int8 gradient
+ * codes (quantized contributions) come from the same sum by an integer
+ * shift; their per-block scales are |N(0, sigma)| draws of a separate key.  Only integer
  * operations and single IEEE binary32 multiplies are used (no contraction is
  * possible), so host and device agree bit for bit.
  */
@@ -35,7 +37,7 @@
 #define ZSG_GOLDEN 0x9E3779B97F4A7C15ull
 
 /* tensor ids */
-enum { ZSG_MASTER = 0, ZSG_MOM = 1, ZSG_VAR = 2, ZSG_GRAD = 3, ZSG_AUX = 4 };
+enum { ZSG_MASTER = 0, ZSG_MOM = 1, ZSG_VAR = 2, ZSG_GRAD = 3, ZSG_AUX = 4, ZSG_GRAD_SCALE = 5 };
 /* output kinds */
 enum { ZSG_KIND_NORMAL = 0, ZSG_KIND_ABS = 1 };
 
@@ -77,6 +79,20 @@ ZSG_FN float zsg_value(uint64_t h, uint64_t i, float sigma, int outliers, int ki
   if (outliers && zsg_is_outlier(h, i)) x = 100.0f * x;
   if (kind == ZSG_KIND_ABS && x < 0.0f) x = -x;
   return x;
+}
+
+/* An int8 code for element i: the same twelve-field sum, centred, divided
+ * by 2^11 with an arithmetic shift (floor), clamped to [-127, 127]:
+ * integers with standard deviation 32 (the shape of block-quantized
+ * gradients whose block absmax sits near 4 sigma).  Integer-only. */
+ZSG_FN int8_t zsg_code(uint64_t h, uint64_t i) {
+  const uint64_t base = h + (4u * i + 1u) * ZSG_GOLDEN;
+  const uint32_t s = zsg_fields4(zsg_mix64(base)) +
+                     zsg_fields4(zsg_mix64(base + ZSG_GOLDEN)) +
+                     zsg_fields4(zsg_mix64(base + 2u * ZSG_GOLDEN));
+  int32_t c = ((int32_t)s - 393210) >> 11;
+  c = c > 127 ? 127 : (c < -127 ? -127 : c);
+  return (int8_t)c;
 }
 
 /* Nearest bf16 (ties to even) of a finite binary32, as a bit pattern. */

@@ -390,3 +390,87 @@ def test_step_empty_shard_and_bad_args():
     with pytest.raises(ValueError):
         O.step([np.zeros(4, np.uint16)], np.zeros(4, np.float32), np.zeros(4, np.float32),
                np.zeros(4, np.float32), O.Hyper(t=0))
+
+
+# ------------------------------------------- a1 with int8 contributions (qgZ)
+
+def test_q8_reduce_exact_audit():
+    """The rank-order binary64 sum of the products code * scale is the exact
+    rational sum on the 64-rank workload's draws, and the average is that
+    sum / N_d rounded once."""
+    w = S.by_name("7.5B-nd64-zeropp")
+    codes, scales = S.host_contrib_q8(w, 1, 256 * 10, 2048 + 100)
+    s = O.reduce_sum_q8(list(codes), list(scales), 256)
+    for i in range(0, codes.shape[1], 11):
+        exact = sum(Fraction(int(codes[k, i])) * Fraction(float(scales[k, i // 256]))
+                    for k in range(w.n_d))
+        assert Fraction(float(s[i])) == exact
+    g = O.reduce_average_q8(list(codes), list(scales), 256)
+    assert np.array_equal(g, (s / w.n_d).astype(np.float32))
+
+
+def test_q8_reduce_matches_bf16_reduce_on_exact_values():
+    """With power-of-two scales every code * scale is an exact bf16 value
+    (|code| <= 127 has at most 7 significant bits), so the int8 front end must
+    agree bit for bit with the pinned bf16 reduce of those values."""
+    rng = np.random.default_rng(3)
+    nd, n, block = 8, 1000, 64
+    codes = rng.integers(-127, 128, size=(nd, n)).astype(np.int8)
+    nb = (n + block - 1) // block
+    scales = np.ldexp(1.0, -rng.integers(5, 30, size=(nd, nb))).astype(np.float32)
+    vals = codes.astype(np.float64) * np.repeat(scales, block, axis=1)[:, :n]
+    rows = [_bf16_bits(vals[k].astype(np.float32)) for k in range(nd)]
+    g8 = O.reduce_average_q8(list(codes), list(scales), block)
+    assert np.array_equal(g8, O.reduce_average(rows))
+
+
+def test_q8_roundtrip_through_the_block_quantizer():
+    """Quantizing each rank's bf16 gradient with the a5 quantizer and reducing
+    the codes lands within the ranks' half quantization steps (averaged) of
+    the bf16 reduce: the two front ends describe the same gradient."""
+    w = S.by_name("gpt2-small-flat")
+    n, block = 5000, 256
+    rows = S.host_contrib(w, 1, 0, n)
+    qs = [O.quant_int8(rows[k], block) for k in range(w.n_d)]
+    g8 = O.reduce_average_q8([c for c, _ in qs], [s for _, s in qs], block)
+    g = O.reduce_average(list(rows))
+    half = sum(np.repeat(s.astype(np.float64), block)[:n] for _, s in qs) / 2 / w.n_d
+    err = np.abs(g8.astype(np.float64) - g.astype(np.float64))
+    assert np.all(err <= half * (1 + 1e-6) + np.spacing(np.abs(g)))
+    assert err.max() > 0  # quantization is not the identity here
+
+
+def test_q8_block_indexing():
+    """A scale in block b of rank k acts on block b's elements of rank k only."""
+    nd, n, block = 4, 320, 32
+    for k, b in [(0, 0), (3, 9), (2, 4)]:
+        codes = [np.ones(n, np.int8) for _ in range(nd)]
+        scales = [np.zeros((n + block - 1) // block, np.float32) for _ in range(nd)]
+        scales[k][b] = 4.0
+        g = O.reduce_average_q8(codes, scales, block)
+        want = np.zeros(n, np.float32)
+        want[b * block:(b + 1) * block] = 1.0
+        assert np.array_equal(g, want)
+
+
+def test_q8_step_equals_step_on_exact_values():
+    """The whole q8 step equals the bf16 step when the values coincide."""
+    rng = np.random.default_rng(5)
+    nd, n, block = 16, 3000, 256
+    codes = rng.integers(-127, 128, size=(nd, n)).astype(np.int8)
+    nb = (n + block - 1) // block
+    scales = np.ldexp(1.0, -rng.integers(14, 18, size=(nd, nb))).astype(np.float32)
+    vals = codes.astype(np.float64) * np.repeat(scales, block, axis=1)[:, :n]
+    rows = [_bf16_bits(vals[k].astype(np.float32)) for k in range(nd)]
+    w = S.by_name("13B-nd16-clip-int8")
+    outs = []
+    for fn in ("q8", "bf16"):
+        master, m, v = S.host_state(w, 0, n)
+        h = O.Hyper(lr=1e-4, weight_decay=0.1, max_norm=0.01, quant_block=256, t=1)
+        o = (O.step_q8(list(codes), list(scales), block, master, m, v, h) if fn == "q8"
+             else O.step(rows, master, m, v, h))
+        outs.append((master, m, v, o))
+    for x, y in zip(outs[0][:3], outs[1][:3]):
+        assert np.array_equal(x, y)
+    assert np.array_equal(outs[0][3].codes, outs[1][3].codes)
+    assert outs[0][3].sumsq == outs[1][3].sumsq

@@ -49,3 +49,14 @@ def test_workload_geometry():
     assert w4.phi == 40 * (4 * 5120 * 5120 + 3 * 5120 * 13824) + 32000 * 5120
     assert w4.phi == 12_851_609_600 and all(s % 128 == 0 for _, s in w4.segments)
     assert [w.bytes_per_param() for w in S.WORKLOADS[:3]] == [34, 42, 154]
+
+
+def test_int8_contributions_shape_and_windows():
+    w = S.by_name("7.5B-nd64-zeropp")
+    c, s = S.host_contrib_q8(w, 2, 0, 256 * 40)
+    assert c.dtype == np.int8 and c.shape == (64, 256 * 40) and s.shape == (64, 40)
+    assert abs(c.astype(np.float64).std() - 32) < 0.5 and np.abs(c).max() <= 127
+    assert (s >= 0).all() and abs(s.mean() / (w.scale_sigma * 0.7979) - 1) < 0.05
+    c2, s2 = S.host_contrib_q8(w, 2, 256 * 7, 256 * 3 + 5)
+    assert np.array_equal(c2, c[:, 256 * 7: 256 * 10 + 5])
+    assert np.array_equal(s2, s[:, 7:11])
