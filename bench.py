@@ -36,13 +36,17 @@ def _eprint(*a):
 
 
 def kernel_bytes(w, spill: bool = True) -> dict[str, float]:
-    """Algorithmic HBM bytes per shard element of each launch of a step."""
+    """Algorithmic HBM bytes per shard element of each launch of a step:
+    contribution rows (2 B bf16, or 1 B int8 + a 4 B scale per block), fp32
+    state in and out, the bf16 copy, int8 codes + scales; with clipping the
+    norm pass writes a 4 B fp32 spill that the update reads."""
     q = (1.0 + 4.0 / w.quant_block) if w.quant_block else 0.0
+    row = (1.0 + 4.0 / w.contrib_block) if w.contrib_block else 2.0
     if w.max_norm > 0:
-        norm = 2.0 * w.n_d + (4.0 if spill else 0.0)        # rows in, fp32 spill out
-        upd = (4.0 if spill else 2.0 * w.n_d) + 24.0 + 2.0 + q  # spill in, state, bf16
+        norm = row * w.n_d + (4.0 if spill else 0.0)
+        upd = (4.0 if spill else row * w.n_d) + 24.0 + 2.0 + q
         return {"gnorm": norm, "step": upd}
-    return {"step": 2.0 * w.n_d + 24.0 + 2.0 + q}
+    return {"step": row * w.n_d + 24.0 + 2.0 + q}
 
 
 def cpu_baseline(w, target_s: float = 12.0, max_n: int = 1 << 27) -> dict:
@@ -153,22 +157,15 @@ def main() -> int:
     kb = kernel_bytes(w, spill)
 
     def one_step(s, ev=None):
-        lr = w.lr
         if g.clip:
             if ev is not None:
                 ev[0].record(stream)
-            g.shard.gnorm(g.rows, g.sumsq)
-            if ev is not None:
-                ev[1].record(stream)
-            g.shard.step(None if g.gbar_ws is not None else g.rows, lr, w.t_of(s), g.sumsq)
-            if ev is not None:
-                ev[2].record(stream)
-        else:
-            if ev is not None:
-                ev[1].record(stream)
-            g.shard.step(g.rows, lr, w.t_of(s))
-            if ev is not None:
-                ev[2].record(stream)
+            g.norm()
+        if ev is not None:
+            ev[1].record(stream)
+        g.update(s)
+        if ev is not None:
+            ev[2].record(stream)
 
     for s in range(1, args.warmup + 1):
         one_step(s)

@@ -37,6 +37,9 @@
  *          a = max |p|, scale = binary32(a / 127), code = round-half-even(
  *          binary32(p / scale)) clamped to +-127; scale 0 => codes 0;
  *          a non-finite quotient gives code 0.
+ * With int8 contributions (the _q8 calls) element i of row k stands for
+ * code_k[i] * scale_k[i / block], an exact binary64 product, and s_i sums
+ * those products in the same k order.
  * Non-finite inputs propagate per IEEE; no step is skipped.
  *
  * Memory: every pointer in zs_desc and every contribution pointer is a
@@ -133,6 +136,19 @@ int zero_shard_gnorm(zs_handle *h, const zs_bf16 *const *contrib, double *sumsq_
  * Errors: ZS_EINVAL, ZS_EALIGN, ZS_ESTATE, ZS_EHIP. */
 int zero_shard_step(zs_handle *h, const zs_bf16 *const *contrib, float lr, int64_t t,
                     const double *global_sumsq_dev);
+
+/* a1 with int8 contributions: ZeRO++ qgZ ("ZeRO (딥 러닝)", follow-ups table
+ * "후속 기법": gradients are quantized and averaged after an all-to-all).
+ * Row k is codes[k], int8[shard_len] (8-byte aligned), with one fp32 scale
+ * per `block` contiguous shard elements starting at element 0, scales[k],
+ * fp32[ceil(shard_len / block)] (4-byte aligned); codes and scales are HOST
+ * arrays of n_d device pointers; block is 32, 64, 128, 256 or 512.
+ * Otherwise exactly zero_shard_gnorm and zero_shard_step (codes and scales
+ * may be NULL when the step reads the gradient spill).  Errors: as there. */
+int zero_shard_gnorm_q8(zs_handle *h, const int8_t *const *codes, const float *const *scales,
+                        int32_t block, double *sumsq_dev);
+int zero_shard_step_q8(zs_handle *h, const int8_t *const *codes, const float *const *scales,
+                       int32_t block, float lr, int64_t t, const double *global_sumsq_dev);
 
 /* a5 as a separate pass: quantize param_out into q_codes / q_scales with
  * the given block (32, 64, 128, 256 or 512); q_scales must hold

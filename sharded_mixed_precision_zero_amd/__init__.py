@@ -65,6 +65,12 @@ _lib.zero_shard_gnorm.argtypes = [_handle_p, ctypes.c_void_p, ctypes.c_void_p]
 _lib.zero_shard_step.restype = ctypes.c_int
 _lib.zero_shard_step.argtypes = [_handle_p, ctypes.c_void_p, ctypes.c_float, ctypes.c_int64,
                                  ctypes.c_void_p]
+_lib.zero_shard_gnorm_q8.restype = ctypes.c_int
+_lib.zero_shard_gnorm_q8.argtypes = [_handle_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
+                                     ctypes.c_void_p]
+_lib.zero_shard_step_q8.restype = ctypes.c_int
+_lib.zero_shard_step_q8.argtypes = [_handle_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
+                                    ctypes.c_float, ctypes.c_int64, ctypes.c_void_p]
 _lib.zero_shard_quant.restype = ctypes.c_int
 _lib.zero_shard_quant.argtypes = [_handle_p, ctypes.c_int32]
 _lib.zero_shard_free.restype = ctypes.c_int
@@ -74,8 +80,9 @@ _lib.zero_shard_strerror.argtypes = [ctypes.c_int]
 _lib.zero_shard_len.restype = ctypes.c_int64
 _lib.zero_shard_len.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32]
 
-EXPORTS = ("zero_shard_init", "zero_shard_gnorm", "zero_shard_step", "zero_shard_quant",
-           "zero_shard_free", "zero_shard_strerror", "zero_shard_len")
+EXPORTS = ("zero_shard_init", "zero_shard_gnorm", "zero_shard_step", "zero_shard_gnorm_q8",
+           "zero_shard_step_q8", "zero_shard_quant", "zero_shard_free", "zero_shard_strerror",
+           "zero_shard_len")
 
 
 class ZeroShardError(RuntimeError):
@@ -96,8 +103,8 @@ def _ptr(t) -> int | None:
 
 
 def contrib_table(contrib) -> ctypes.Array | None:
-    """Host array of device pointers: a list of 1-D 16-bit tensors, or the
-    rows of a 2-D 16-bit tensor (row k = rank k's contribution)."""
+    """Host array of device pointers: a list of 1-D tensors (or None), or the
+    rows of a 2-D tensor (row k = rank k's contribution, codes or scales)."""
     if contrib is None:
         return None
     if hasattr(contrib, "dim") and contrib.dim() == 2:
@@ -132,6 +139,17 @@ def zero_shard_gnorm(h, contrib, sumsq_dev) -> int:
 def zero_shard_step(h, contrib, lr: float, t: int, global_sumsq_dev=None) -> int:
     return _lib.zero_shard_step(h, contrib_table(contrib), float(lr), int(t),
                                 _ptr(global_sumsq_dev))
+
+
+def zero_shard_gnorm_q8(h, codes, scales, block: int, sumsq_dev) -> int:
+    return _lib.zero_shard_gnorm_q8(h, contrib_table(codes), contrib_table(scales), int(block),
+                                    _ptr(sumsq_dev))
+
+
+def zero_shard_step_q8(h, codes, scales, block: int, lr: float, t: int,
+                       global_sumsq_dev=None) -> int:
+    return _lib.zero_shard_step_q8(h, contrib_table(codes), contrib_table(scales), int(block),
+                                   float(lr), int(t), _ptr(global_sumsq_dev))
 
 
 def zero_shard_quant(h, block: int) -> int:
@@ -178,6 +196,13 @@ class ZeroShard:
 
     def step(self, contrib, lr: float, t: int, global_sumsq_dev=None) -> None:
         _check(zero_shard_step(self.h, contrib, lr, t, global_sumsq_dev), "zero_shard_step")
+
+    def gnorm_q8(self, codes, scales, block: int, sumsq_dev) -> None:
+        _check(zero_shard_gnorm_q8(self.h, codes, scales, block, sumsq_dev), "zero_shard_gnorm_q8")
+
+    def step_q8(self, codes, scales, block: int, lr: float, t: int, global_sumsq_dev=None) -> None:
+        _check(zero_shard_step_q8(self.h, codes, scales, block, lr, t, global_sumsq_dev),
+               "zero_shard_step_q8")
 
     def quant(self, block: int) -> None:
         _check(zero_shard_quant(self.h, block), "zero_shard_quant")

@@ -47,10 +47,13 @@ constexpr int kVec = 8;          // shard elements per lane
 #define ZS_ROW_GROUP 8
 #endif
 constexpr int kRowGroup = ZS_ROW_GROUP;  // contribution rows loaded together (update)
+#ifndef ZS_WIDE_ROW_GROUP
+#define ZS_WIDE_ROW_GROUP 4
+#endif
 #ifndef ZS_NORM_ROW_GROUP
 #define ZS_NORM_ROW_GROUP 4
 #endif
-constexpr int kNormRowGroup = ZS_NORM_ROW_GROUP;  // rows loaded together (norm pass)
+
 #ifndef ZS_NORM_BLOCKS
 #define ZS_NORM_BLOCKS 16384
 #endif
@@ -58,7 +61,7 @@ constexpr int kNormBlocks = ZS_NORM_BLOCKS;  // fixed grid of the norm pass
 #ifndef ZS_NORM_UNROLL
 #define ZS_NORM_UNROLL 4
 #endif
-constexpr int kNormUnroll = ZS_NORM_UNROLL;  // lane-vectors per lane per sweep
+
 #ifndef ZS_BLOCKS_PER_CU
 #define ZS_BLOCKS_PER_CU 0
 #endif
@@ -69,8 +72,42 @@ constexpr int kNormUnroll = ZS_NORM_UNROLL;  // lane-vectors per lane per sweep
 #define ZS_NT_SPILL 0
 #endif
 
-struct Rows {
-  const u32x4 *p[ZS_MAX_ND];  // row k = rank k's contribution for this shard
+// Contribution sources: row k is rank k's gradient for this shard.
+struct Bf16Rows {
+  const u32x4 *p[ZS_MAX_ND];  // bf16: 8 elements per 16-byte load
+};
+struct Q8Rows {
+  const u32x2 *c[ZS_MAX_ND];  // int8 codes: 8 elements per 8-byte load
+  const float *s[ZS_MAX_ND];  // one fp32 scale per block of the row
+  int32_t shift;              // log2(lane-vectors per block)
+};
+
+#ifndef ZS_Q8_WIDE_UNROLL
+#define ZS_Q8_WIDE_UNROLL 4
+#endif
+#ifndef ZS_Q8_WIDE_GROUP
+#define ZS_Q8_WIDE_GROUP 2
+#endif
+#ifndef ZS_Q8_NORM_UNROLL
+#define ZS_Q8_NORM_UNROLL 2
+#endif
+#ifndef ZS_Q8_NORM_GROUP
+#define ZS_Q8_NORM_GROUP 4
+#endif
+
+// Launch shape per contribution format: lane-vectors per wave sweep and rows
+// loaded together, for the wide update and for the norm pass.
+template <class Src>
+struct Tune;
+template <>
+struct Tune<Bf16Rows> {
+  static constexpr int wide_unroll = 4, wide_group = ZS_WIDE_ROW_GROUP;
+  static constexpr int norm_unroll = ZS_NORM_UNROLL, norm_group = ZS_NORM_ROW_GROUP;
+};
+template <>
+struct Tune<Q8Rows> {
+  static constexpr int wide_unroll = ZS_Q8_WIDE_UNROLL, wide_group = ZS_Q8_WIDE_GROUP;
+  static constexpr int norm_unroll = ZS_Q8_NORM_UNROLL, norm_group = ZS_Q8_NORM_GROUP;
 };
 
 struct AdamConst {
@@ -86,8 +123,9 @@ struct Avg {
   double nd_f, inv_nd;
 };
 
+template <class Src>
 struct StepArgs {
-  Rows rows;
+  Src src;
   Avg avg;
   AdamConst k;
   int64_t n;
@@ -100,8 +138,9 @@ struct StepArgs {
   float *scales;
 };
 
+template <class Src>
 struct NormArgs {
-  Rows rows;
+  Src src;
   Avg avg;
   int64_t n;
   float *gbar_out;   // store the averaged gradient iff non-null
@@ -151,37 +190,90 @@ __device__ __forceinline__ void add_row(double (&s)[kVec], const u32x4 r) {
   s[7] += static_cast<double>(bf16_hi(r.w));
 }
 
+// One full lane-vector of row k, and its addition into the per-element
+// binary64 sums.  bf16: the value itself; int8: code * scale, an exact
+// product in binary64.
+struct Bf16Frag {
+  u32x4 r;
+};
+struct Q8Frag {
+  u32x2 c;
+  float s;
+};
+
+__device__ __forceinline__ Bf16Frag fetch(const Bf16Rows &src, int k, int64_t vec) {
+  return {__builtin_nontemporal_load(src.p[k] + vec)};
+}
+
+__device__ __forceinline__ Q8Frag fetch(const Q8Rows &src, int k, int64_t vec) {
+  return {__builtin_nontemporal_load(src.c[k] + vec), src.s[k][vec >> src.shift]};
+}
+
+__device__ __forceinline__ void accum(double (&s)[kVec], const Bf16Frag &f) { add_row(s, f.r); }
+
+// s + code * scale.  The product of an int8 and a binary32 is exact in
+// binary64, so one fused multiply-add rounds exactly as the product followed
+// by the addition does, with one instruction instead of two.
+__device__ __forceinline__ double add_dequant(double s, unsigned w, int byte, double scale) {
+  return __builtin_fma(static_cast<double>(static_cast<int8_t>(w >> (8 * byte))), scale, s);
+}
+
+__device__ __forceinline__ void accum(double (&s)[kVec], const Q8Frag &f) {
+  const double sc = static_cast<double>(f.s);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    s[e] = add_dequant(s[e], f.c.x, e, sc);
+    s[e + 4] = add_dequant(s[e + 4], f.c.y, e, sc);
+  }
+}
+
+// The first nvalid elements of lane-vector vec of row k (the shard's last,
+// partial vector), element by element.
+__device__ __forceinline__ void accum_partial(double (&s)[kVec], const Bf16Rows &src, int k,
+                                              int64_t vec, int nvalid) {
+  const uint16_t *row = reinterpret_cast<const uint16_t *>(src.p[k]) + vec * kVec;
+#pragma unroll
+  for (int e = 0; e < kVec; ++e)
+    if (e < nvalid) s[e] += static_cast<double>(__uint_as_float(unsigned(row[e]) << 16));
+}
+
+__device__ __forceinline__ void accum_partial(double (&s)[kVec], const Q8Rows &src, int k,
+                                              int64_t vec, int nvalid) {
+  const int8_t *row = reinterpret_cast<const int8_t *>(src.c[k]) + vec * kVec;
+  const double sc = static_cast<double>(src.s[k][vec >> src.shift]);
+#pragma unroll
+  for (int e = 0; e < kVec; ++e)
+    if (e < nvalid) s[e] = __builtin_fma(static_cast<double>(row[e]), sc, s[e]);
+}
+
 __device__ __forceinline__ float average(double s, const Avg &a) {
   return a.pow2 ? static_cast<float>(s * a.inv_nd) : static_cast<float>(s / a.nd_f);
 }
 
 // Averaged gradient of the 8 elements of lane-vector `vec`.  Full vectors
-// take 128-bit loads, rows in groups of kRowGroup; a partial vector (the
-// shard's last, nvalid < 8) loads element by element.  The additions are
-// the same in both cases: k = 0..nd-1 into a binary64 accumulator per
-// element.
-__device__ __forceinline__ void reduce_average(const Rows &rows, const Avg &avg, int64_t vec,
+// take one vector load per row, rows in groups of kRowGroup; a partial
+// vector (the shard's last, nvalid < 8) loads element by element.  The
+// additions are the same in both cases: k = 0..nd-1 into a binary64
+// accumulator per element.
+template <class Src>
+__device__ __forceinline__ void reduce_average(const Src &src, const Avg &avg, int64_t vec,
                                                int nvalid, float (&g)[kVec]) {
+  using Frag = decltype(fetch(src, 0, 0));
   double s[kVec];
 #pragma unroll
   for (int e = 0; e < kVec; ++e) s[e] = 0.0;
   if (nvalid == kVec) {
     for (int k0 = 0; k0 < avg.nd; k0 += kRowGroup) {
-      u32x4 r[kRowGroup];
+      Frag r[kRowGroup];
 #pragma unroll
       for (int j = 0; j < kRowGroup; ++j)
-        if (k0 + j < avg.nd) r[j] = __builtin_nontemporal_load(rows.p[k0 + j] + vec);
+        if (k0 + j < avg.nd) r[j] = fetch(src, k0 + j, vec);
 #pragma unroll
       for (int j = 0; j < kRowGroup; ++j)
-        if (k0 + j < avg.nd) add_row(s, r[j]);
+        if (k0 + j < avg.nd) accum(s, r[j]);
     }
   } else {
-    for (int k = 0; k < avg.nd; ++k) {
-      const uint16_t *row = reinterpret_cast<const uint16_t *>(rows.p[k]) + vec * kVec;
-#pragma unroll
-      for (int e = 0; e < kVec; ++e)
-        if (e < nvalid) s[e] += static_cast<double>(__uint_as_float(unsigned(row[e]) << 16));
-    }
+    for (int k = 0; k < avg.nd; ++k) accum_partial(s, src, k, vec, nvalid);
   }
 #pragma unroll
   for (int e = 0; e < kVec; ++e) g[e] = average(s[e], avg);
@@ -261,27 +353,27 @@ __device__ __forceinline__ void quant_lane(const float (&p)[kVec], int nvalid, i
 // Averaged gradient of the U full lane-vectors v0, v0+64, .., v0+64(U-1)
 // (one per wave-sweep of 64 lanes): U*kRowGroup 16-byte loads in flight per
 // lane; per element the same k-ordered binary64 sum as reduce_average.
-template <int U, int G>
-__device__ __forceinline__ void reduce_average_wave(const Rows &rows, const Avg &avg, int64_t v0,
+template <int U, int G, class Src>
+__device__ __forceinline__ void reduce_average_wave(const Src &src, const Avg &avg, int64_t v0,
                                                     float (&g)[U][kVec]) {
+  using Frag = decltype(fetch(src, 0, 0));
   double s[U][kVec];
 #pragma unroll
   for (int u = 0; u < U; ++u)
 #pragma unroll
     for (int e = 0; e < kVec; ++e) s[u][e] = 0.0;
   for (int k0 = 0; k0 < avg.nd; k0 += G) {
-    u32x4 r[U][G];
+    Frag r[U][G];
 #pragma unroll
     for (int j = 0; j < G; ++j)
       if (k0 + j < avg.nd)
 #pragma unroll
-        for (int u = 0; u < U; ++u)
-          r[u][j] = __builtin_nontemporal_load(rows.p[k0 + j] + v0 + 64 * u);
+        for (int u = 0; u < U; ++u) r[u][j] = fetch(src, k0 + j, v0 + 64 * u);
 #pragma unroll
     for (int j = 0; j < G; ++j)
       if (k0 + j < avg.nd)
 #pragma unroll
-        for (int u = 0; u < U; ++u) add_row(s[u], r[u][j]);
+        for (int u = 0; u < U; ++u) accum(s[u], r[u][j]);
   }
 #pragma unroll
   for (int u = 0; u < U; ++u)
@@ -292,8 +384,8 @@ __device__ __forceinline__ void reduce_average_wave(const Rows &rows, const Avg 
 // One lane-vector (8 elements) of the update, any fill level: nvalid = 0..8
 // valid elements.  Every lane of the wave calls it together (the quantizer
 // reduces across lanes); lanes past the end pass a vector with nvalid 0.
-template <int QL>
-__device__ __forceinline__ void step_vec(const StepArgs &A, int64_t vec, double coef) {
+template <int QL, class Src>
+__device__ __forceinline__ void step_vec(const StepArgs<Src> &A, int64_t vec, double coef) {
     const int64_t e0 = vec * kVec;
     const int nvalid = e0 + kVec <= A.n ? kVec : (e0 < A.n ? int(A.n - e0) : 0);
     float th[kVec], mo[kVec], va[kVec], g[kVec], p[kVec];
@@ -331,7 +423,7 @@ __device__ __forceinline__ void step_vec(const StepArgs &A, int64_t vec, double 
           for (int e = 0; e < kVec; ++e) g[e] = e < nvalid ? A.gbar[e0 + e] : 0.0f;
         }
       } else {
-        reduce_average(A.rows, A.avg, vec, nvalid, g);
+        reduce_average(A.src, A.avg, vec, nvalid, g);
       }
 #pragma unroll
       for (int e = 0; e < kVec; ++e) {
@@ -380,12 +472,7 @@ __device__ __forceinline__ void step_vec(const StepArgs &A, int64_t vec, double 
 #ifndef ZS_WIDE_MIN_ROWS
 #define ZS_WIDE_MIN_ROWS 16
 #endif
-#ifndef ZS_WIDE_ROW_GROUP
-#define ZS_WIDE_ROW_GROUP 4
-#endif
-constexpr int kWideMinRows = ZS_WIDE_MIN_ROWS;    // rows from which the update goes wide
-constexpr int kWideUnroll = 4;                    // lane-vectors per wave sweep when wide
-constexpr int kWideRowGroup = ZS_WIDE_ROW_GROUP;  // rows loaded together when wide
+constexpr int kWideMinRows = ZS_WIDE_MIN_ROWS;  // rows from which the update goes wide
 
 // a1 + a2 (apply) + a3 + a4 (+ a5 when QL > 0).  Each wave owns a chunk of
 // 64*U consecutive lane-vectors per iteration (lane l takes v0+l, v0+64+l,
@@ -395,8 +482,8 @@ constexpr int kWideRowGroup = ZS_WIDE_ROW_GROUP;  // rows loaded together when w
 // loads in flight, then each vector's state is updated in turn.  The
 // shard's last, partial chunk goes vector by vector.  The loop condition is
 // uniform across the wave, as the quantizer's shuffles need.
-template <int QL, int U>
-__global__ void __launch_bounds__(kThreads) step_kernel(const StepArgs A) {
+template <int QL, int U, class Src>
+__global__ void __launch_bounds__(kThreads) step_kernel(const StepArgs<Src> A) {
   constexpr int64_t span = 64 * U;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -409,11 +496,11 @@ __global__ void __launch_bounds__(kThreads) step_kernel(const StepArgs A) {
        wb += stride) {
     if (U == 1 || wb + span > nfull) {
 #pragma unroll
-      for (int u = 0; u < U; ++u) step_vec<QL>(A, wb + 64 * u + lane, coef);
+      for (int u = 0; u < U; ++u) step_vec<QL, Src>(A, wb + 64 * u + lane, coef);
       continue;
     }
     float g[U][kVec];
-    reduce_average_wave<U, kWideRowGroup>(A.rows, A.avg, wb + lane, g);
+    reduce_average_wave<U, Tune<Src>::wide_group>(A.src, A.avg, wb + lane, g);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t vec = wb + 64 * u + lane;
@@ -474,12 +561,13 @@ __device__ __forceinline__ void store_gbar(float *out, int64_t vec, int nvalid,
 }
 
 // a2, first kernel: block partial sums of gbar^2 (binary64).  The grid is
-// fixed by n alone.  Each wave sweeps 64*kNormUnroll consecutive
+// fixed by n alone.  Each wave sweeps 64*U (U per contribution format) consecutive
 // lane-vectors per iteration (lane l takes v0+l, v0+64+l, ...); a lane's
 // sum runs over its vectors in sweep order, then a fixed butterfly over
 // the wave and the 4 wave sums in order.
-__global__ void __launch_bounds__(kThreads) gnorm_partial_kernel(const NormArgs A) {
-  constexpr int U = kNormUnroll;
+template <class Src>
+__global__ void __launch_bounds__(kThreads) gnorm_partial_kernel(const NormArgs<Src> A) {
+  constexpr int U = Tune<Src>::norm_unroll;
   constexpr int64_t span = 64 * U;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -491,7 +579,7 @@ __global__ void __launch_bounds__(kThreads) gnorm_partial_kernel(const NormArgs 
        wb += stride) {
     if (wb + span <= nfull) {
       float g[U][kVec];
-      reduce_average_wave<U, kNormRowGroup>(A.rows, A.avg, wb + lane, g);
+      reduce_average_wave<U, Tune<Src>::norm_group>(A.src, A.avg, wb + lane, g);
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         if (A.gbar_out) store_gbar(A.gbar_out, wb + 64 * u + lane, kVec, g[u]);
@@ -508,7 +596,7 @@ __global__ void __launch_bounds__(kThreads) gnorm_partial_kernel(const NormArgs 
         const int64_t e0 = vec * kVec;
         const int nvalid = e0 + kVec <= A.n ? kVec : int(A.n - e0);
         float g[kVec];
-        reduce_average(A.rows, A.avg, vec, nvalid, g);
+        reduce_average(A.src, A.avg, vec, nvalid, g);
         if (A.gbar_out) store_gbar(A.gbar_out, vec, nvalid, g);
 #pragma unroll
         for (int e = 0; e < kVec; ++e) {
@@ -635,13 +723,27 @@ Avg make_avg(int32_t nd) {
   return a;
 }
 
-int check_rows(const zs_handle *h, const zs_bf16 *const *contrib, Rows *rows) {
+int check_rows(const zs_handle *h, const zs_bf16 *const *contrib, Bf16Rows *src) {
   if (!contrib) return ZS_EINVAL;
-  std::memset(rows, 0, sizeof *rows);
   for (int k = 0; k < h->d.n_d; ++k) {
     if (!contrib[k]) return ZS_EINVAL;
     if (!aligned(contrib[k], 16)) return ZS_EALIGN;
-    rows->p[k] = reinterpret_cast<const u32x4 *>(contrib[k]);
+    src->p[k] = reinterpret_cast<const u32x4 *>(contrib[k]);
+  }
+  return ZS_OK;
+}
+
+int check_q8(const zs_handle *h, const int8_t *const *codes, const float *const *scales,
+             int32_t block, Q8Rows *src) {
+  const int lanes = quant_lanes(block);
+  if (lanes < 0 || !codes || !scales) return ZS_EINVAL;
+  src->shift = 0;
+  while ((1 << src->shift) < lanes) ++src->shift;
+  for (int k = 0; k < h->d.n_d; ++k) {
+    if (!codes[k] || !scales[k]) return ZS_EINVAL;
+    if (!aligned(codes[k], 8) || !aligned(scales[k], 4)) return ZS_EALIGN;
+    src->c[k] = reinterpret_cast<const u32x2 *>(codes[k]);
+    src->s[k] = scales[k];
   }
   return ZS_OK;
 }
@@ -653,6 +755,114 @@ int current_device_ok(const zs_handle *h) {
 }
 
 int launched() { return hipGetLastError() == hipSuccess ? ZS_OK : ZS_EHIP; }
+
+int gnorm_args_ok(zs_handle *h, double *sumsq_dev) {
+  if (!live(h)) return ZS_ESTATE;
+  if (!sumsq_dev) return ZS_EINVAL;
+  if (!aligned(sumsq_dev, 8)) return ZS_EALIGN;
+  return ZS_OK;
+}
+
+// a2, first sweep, after the contributions were checked: block partials,
+// then the fixed-order final reduction into *sumsq_dev.
+template <class Src>
+int run_gnorm(zs_handle *h, const Src &src, double *sumsq_dev) {
+  int rc = current_device_ok(h);
+  if (rc) return rc;
+  const int64_t n = h->d.shard_len;
+  const hipStream_t st = static_cast<hipStream_t>(h->d.stream);
+  const int64_t nvec = (n + kVec - 1) / kVec;
+  const int64_t per_block = int64_t(kThreads) * Tune<Src>::norm_unroll;
+  int64_t blocks = (nvec + per_block - 1) / per_block;
+  if (blocks > kNormBlocks) blocks = kNormBlocks;
+  if (blocks < 1) blocks = 1;
+  NormArgs<Src> A;
+  A.src = src;
+  A.avg = make_avg(h->d.n_d);
+  A.n = n;
+  A.gbar_out = h->d.gbar_ws;
+  A.partials = h->partials;
+  hipLaunchKernelGGL(gnorm_partial_kernel<Src>, dim3(unsigned(blocks)), dim3(kThreads), 0, st,
+                     A);
+  if ((rc = launched())) return rc;
+  hipLaunchKernelGGL(gnorm_final_kernel, dim3(1), dim3(kFinalThreads), 0, st,
+                     static_cast<const double *>(h->partials), int(blocks), sumsq_dev);
+  if ((rc = launched())) return rc;
+  h->spill_valid = h->d.gbar_ws != nullptr;
+  return ZS_OK;
+}
+
+int step_args_ok(zs_handle *h, float lr, int64_t t, const double *global_sumsq_dev,
+                 bool *use_spill) {
+  if (!live(h)) return ZS_ESTATE;
+  const zs_desc &d = h->d;
+  if (!(lr >= 0.0f) || !is_finite(lr) || t < 1) return ZS_EINVAL;
+  const bool clip = d.max_norm > 0.0f;
+  if (clip && !global_sumsq_dev) return ZS_EINVAL;
+  if (clip && !aligned(global_sumsq_dev, 8)) return ZS_EALIGN;
+  *use_spill = clip && d.gbar_ws;
+  if (*use_spill && !h->spill_valid) return ZS_ESTATE;
+  return ZS_OK;
+}
+
+// a1 + a2 (apply) + a3 + a4 (+ a5), after the arguments were checked.
+template <class Src>
+int run_step(zs_handle *h, const Src &src, float lr, int64_t t, const double *global_sumsq_dev,
+             bool use_spill) {
+  int rc = current_device_ok(h);
+  if (rc) return rc;
+  const zs_desc &d = h->d;
+  h->spill_valid = false;
+  const int64_t n = d.shard_len;
+  if (n == 0) return ZS_OK;
+  const bool clip = d.max_norm > 0.0f;
+  StepArgs<Src> A;
+  A.src = src;
+  A.avg = make_avg(d.n_d);
+  const double b1 = d.beta1, b2 = d.beta2;
+  A.k.b1 = b1;
+  A.k.omb1 = 1.0 - b1;
+  A.k.b2 = b2;
+  A.k.omb2 = 1.0 - b2;
+  A.k.bc1 = d.bias_correction ? 1.0 - std::pow(b1, double(t)) : 1.0;
+  A.k.bc2 = d.bias_correction ? 1.0 - std::pow(b2, double(t)) : 1.0;
+  A.k.lr = double(lr);
+  A.k.decay = double(lr) * double(d.weight_decay);
+  A.k.eps = double(d.eps);
+  A.n = n;
+  A.sumsq = clip ? global_sumsq_dev : nullptr;
+  A.max_norm = double(d.max_norm);
+  A.gbar = use_spill ? d.gbar_ws : nullptr;
+  A.master = d.master;
+  A.m = d.m;
+  A.v = d.v;
+  A.pout = d.param_out;
+  A.codes = d.q_codes;
+  A.scales = d.q_scales;
+  const hipStream_t st = static_cast<hipStream_t>(d.stream);
+  const int64_t nvec = (n + kVec - 1) / kVec;
+  const bool wide = !A.gbar && d.n_d >= kWideMinRows;
+  constexpr int WU = Tune<Src>::wide_unroll;
+  const dim3 grid(unsigned(grid_blocks(h, nvec, wide ? WU : 1))), block(kThreads);
+#define ZS_LAUNCH_STEP(QL)                                                            \
+  do {                                                                                \
+    if (wide)                                                                         \
+      hipLaunchKernelGGL((step_kernel<QL, WU, Src>), grid, block, 0, st, A);          \
+    else                                                                              \
+      hipLaunchKernelGGL((step_kernel<QL, 1, Src>), grid, block, 0, st, A);           \
+  } while (0)
+  switch (d.quant_block) {
+    case 0: ZS_LAUNCH_STEP(0); break;
+    case 32: ZS_LAUNCH_STEP(4); break;
+    case 64: ZS_LAUNCH_STEP(8); break;
+    case 128: ZS_LAUNCH_STEP(16); break;
+    case 256: ZS_LAUNCH_STEP(32); break;
+    case 512: ZS_LAUNCH_STEP(64); break;
+    default: return ZS_EINVAL;
+  }
+#undef ZS_LAUNCH_STEP
+  return launched();
+}
 
 }  // namespace
 
@@ -730,101 +940,46 @@ int zero_shard_init(const zs_desc *d, zs_handle **out) {
 }
 
 int zero_shard_gnorm(zs_handle *h, const zs_bf16 *const *contrib, double *sumsq_dev) {
-  if (!live(h)) return ZS_ESTATE;
-  if (!sumsq_dev) return ZS_EINVAL;
-  if (!aligned(sumsq_dev, 8)) return ZS_EALIGN;
-  const int64_t n = h->d.shard_len;
-  NormArgs A;
-  std::memset(&A.rows, 0, sizeof A.rows);
-  if (n > 0) {
-    const int rc = check_rows(h, contrib, &A.rows);
-    if (rc) return rc;
-  }
-  int rc = current_device_ok(h);
+  Bf16Rows src;
+  std::memset(&src, 0, sizeof src);
+  int rc = gnorm_args_ok(h, sumsq_dev);
   if (rc) return rc;
-  const hipStream_t st = static_cast<hipStream_t>(h->d.stream);
-  const int64_t nvec = (n + kVec - 1) / kVec;
-  const int64_t per_block = int64_t(kThreads) * kNormUnroll;
-  int64_t blocks = (nvec + per_block - 1) / per_block;
-  if (blocks > kNormBlocks) blocks = kNormBlocks;
-  if (blocks < 1) blocks = 1;
-  A.avg = make_avg(h->d.n_d);
-  A.n = n;
-  A.gbar_out = h->d.gbar_ws;
-  A.partials = h->partials;
-  hipLaunchKernelGGL(gnorm_partial_kernel, dim3(unsigned(blocks)), dim3(kThreads), 0, st, A);
-  if ((rc = launched())) return rc;
-  hipLaunchKernelGGL(gnorm_final_kernel, dim3(1), dim3(kFinalThreads), 0, st,
-                     static_cast<const double *>(h->partials), int(blocks), sumsq_dev);
-  if ((rc = launched())) return rc;
-  h->spill_valid = h->d.gbar_ws != nullptr;
-  return ZS_OK;
+  if (h->d.shard_len > 0 && (rc = check_rows(h, contrib, &src))) return rc;
+  return run_gnorm(h, src, sumsq_dev);
+}
+
+int zero_shard_gnorm_q8(zs_handle *h, const int8_t *const *codes, const float *const *scales,
+                        int32_t block, double *sumsq_dev) {
+  Q8Rows src;
+  std::memset(&src, 0, sizeof src);
+  int rc = gnorm_args_ok(h, sumsq_dev);
+  if (rc) return rc;
+  if (quant_lanes(block) < 0) return ZS_EINVAL;
+  if (h->d.shard_len > 0 && (rc = check_q8(h, codes, scales, block, &src))) return rc;
+  return run_gnorm(h, src, sumsq_dev);
 }
 
 int zero_shard_step(zs_handle *h, const zs_bf16 *const *contrib, float lr, int64_t t,
                     const double *global_sumsq_dev) {
-  if (!live(h)) return ZS_ESTATE;
-  const zs_desc &d = h->d;
-  if (!(lr >= 0.0f) || !is_finite(lr) || t < 1) return ZS_EINVAL;
-  const bool clip = d.max_norm > 0.0f;
-  if (clip && !global_sumsq_dev) return ZS_EINVAL;
-  if (clip && !aligned(global_sumsq_dev, 8)) return ZS_EALIGN;
-  const bool use_spill = clip && d.gbar_ws;
-  if (use_spill && !h->spill_valid) return ZS_ESTATE;
-  const int64_t n = d.shard_len;
-  StepArgs A;
-  std::memset(&A.rows, 0, sizeof A.rows);
-  if (n > 0 && !use_spill) {
-    const int rc = check_rows(h, contrib, &A.rows);
-    if (rc) return rc;
-  }
-  int rc = current_device_ok(h);
+  Bf16Rows src;
+  std::memset(&src, 0, sizeof src);
+  bool spill = false;
+  int rc = step_args_ok(h, lr, t, global_sumsq_dev, &spill);
   if (rc) return rc;
-  h->spill_valid = false;
-  if (n == 0) return ZS_OK;
-  A.avg = make_avg(d.n_d);
-  const double b1 = d.beta1, b2 = d.beta2;
-  A.k.b1 = b1;
-  A.k.omb1 = 1.0 - b1;
-  A.k.b2 = b2;
-  A.k.omb2 = 1.0 - b2;
-  A.k.bc1 = d.bias_correction ? 1.0 - std::pow(b1, double(t)) : 1.0;
-  A.k.bc2 = d.bias_correction ? 1.0 - std::pow(b2, double(t)) : 1.0;
-  A.k.lr = double(lr);
-  A.k.decay = double(lr) * double(d.weight_decay);
-  A.k.eps = double(d.eps);
-  A.n = n;
-  A.sumsq = clip ? global_sumsq_dev : nullptr;
-  A.max_norm = double(d.max_norm);
-  A.gbar = use_spill ? d.gbar_ws : nullptr;
-  A.master = d.master;
-  A.m = d.m;
-  A.v = d.v;
-  A.pout = d.param_out;
-  A.codes = d.q_codes;
-  A.scales = d.q_scales;
-  const hipStream_t st = static_cast<hipStream_t>(d.stream);
-  const int64_t nvec = (n + kVec - 1) / kVec;
-  const bool wide = !A.gbar && d.n_d >= kWideMinRows;
-  const dim3 grid(unsigned(grid_blocks(h, nvec, wide ? kWideUnroll : 1))), block(kThreads);
-#define ZS_LAUNCH_STEP(QL)                                                           \
-  do {                                                                               \
-    if (wide)                                                                        \
-      hipLaunchKernelGGL((step_kernel<QL, kWideUnroll>), grid, block, 0, st, A);     \
-    else                                                                             \
-      hipLaunchKernelGGL((step_kernel<QL, 1>), grid, block, 0, st, A);               \
-  } while (0)
-  switch (d.quant_block) {
-    case 0: ZS_LAUNCH_STEP(0); break;
-    case 32: ZS_LAUNCH_STEP(4); break;
-    case 64: ZS_LAUNCH_STEP(8); break;
-    case 128: ZS_LAUNCH_STEP(16); break;
-    case 256: ZS_LAUNCH_STEP(32); break;
-    case 512: ZS_LAUNCH_STEP(64); break;
-    default: return ZS_EINVAL;
-  }
-#undef ZS_LAUNCH_STEP
-  return launched();
+  if (h->d.shard_len > 0 && !spill && (rc = check_rows(h, contrib, &src))) return rc;
+  return run_step(h, src, lr, t, global_sumsq_dev, spill);
+}
+
+int zero_shard_step_q8(zs_handle *h, const int8_t *const *codes, const float *const *scales,
+                       int32_t block, float lr, int64_t t, const double *global_sumsq_dev) {
+  Q8Rows src;
+  std::memset(&src, 0, sizeof src);
+  bool spill = false;
+  int rc = step_args_ok(h, lr, t, global_sumsq_dev, &spill);
+  if (rc) return rc;
+  if (!spill && quant_lanes(block) < 0) return ZS_EINVAL;
+  if (h->d.shard_len > 0 && !spill && (rc = check_q8(h, codes, scales, block, &src))) return rc;
+  return run_step(h, src, lr, t, global_sumsq_dev, spill);
 }
 
 int zero_shard_quant(zs_handle *h, int32_t block) {

@@ -60,9 +60,23 @@ class GpuShard:
         self.gbar_ws = torch.empty(n_, **f32) if (self.clip and spill) else None
         self.sumsq = torch.zeros(1, dtype=torch.float64, device=DEV)
         self.stride = row_stride(n_)
-        self.rows_buf = torch.empty(max(1, (self.nd - 1) * self.stride + n_), dtype=torch.int16,
-                                    device=DEV)
-        self.rows = [self.rows_buf[k * self.stride: k * self.stride + n_] for k in range(self.nd)]
+        self.cb = w.contrib_block
+        if self.cb:  # int8 contributions: codes rows and per-block scale rows
+            nb = (n_ + self.cb - 1) // self.cb
+            self.sstride = (nb + 63) // 64 * 64 + 64
+            self.codes_buf = torch.empty(max(1, (self.nd - 1) * self.stride + n_),
+                                         dtype=torch.int8, device=DEV)
+            self.scales_buf = torch.empty(max(1, (self.nd - 1) * self.sstride + nb), **f32)
+            self.qrows = [self.codes_buf[k * self.stride: k * self.stride + n_]
+                          for k in range(self.nd)]
+            self.srows = [self.scales_buf[k * self.sstride: k * self.sstride + nb]
+                          for k in range(self.nd)]
+            self.rows_buf = self.rows = None
+        else:
+            self.rows_buf = torch.empty(max(1, (self.nd - 1) * self.stride + n_),
+                                        dtype=torch.int16, device=DEV)
+            self.rows = [self.rows_buf[k * self.stride: k * self.stride + n_]
+                         for k in range(self.nd)]
         if phi is None:
             phi, r = (w.phi, w.r) if n is None else (n_, 0)
         self.shard = Z.ZeroShard(
@@ -77,17 +91,36 @@ class GpuShard:
         S.dev_state(self.w, self.master, self.m, self.v, i0=self.i0)
 
     def fill_grads(self, s: int) -> None:
-        S.dev_contrib(self.w, s, self.rows_buf, self.n, self.stride, i0=self.i0)
+        if self.cb:
+            S.dev_contrib_q8(self.w, s, self.codes_buf, self.scales_buf, self.n, self.stride,
+                             self.sstride, i0=self.i0)
+        else:
+            S.dev_contrib(self.w, s, self.rows_buf, self.n, self.stride, i0=self.i0)
+
+    def norm(self) -> None:
+        """The clipped step's first sweep: this shard's sum of squares into
+        self.sumsq (and the gradient spill when there is one)."""
+        if self.cb:
+            self.shard.gnorm_q8(self.qrows, self.srows, self.cb, self.sumsq)
+        else:
+            self.shard.gnorm(self.rows, self.sumsq)
+
+    def update(self, s: int, lr: float | None = None) -> None:
+        """The update of step s (1-based) on the resident contributions."""
+        lr = self.w.lr if lr is None else lr
+        spill = self.clip and self.gbar_ws is not None
+        ssq = self.sumsq if self.clip else None
+        if self.cb:
+            self.shard.step_q8(None if spill else self.qrows, None if spill else self.srows,
+                               self.cb, lr, self.w.t_of(s), ssq)
+        else:
+            self.shard.step(None if spill else self.rows, lr, self.w.t_of(s), ssq)
 
     def step(self, s: int, lr: float | None = None) -> None:
-        """Step s (1-based) on the resident contributions."""
-        lr = self.w.lr if lr is None else lr
+        """Step s (1-based): the norm sweep when clipping, then the update."""
         if self.clip:
-            self.shard.gnorm(self.rows, self.sumsq)
-            self.shard.step(None if self.gbar_ws is not None else self.rows, lr,
-                            self.w.t_of(s), self.sumsq)
-        else:
-            self.shard.step(self.rows, lr, self.w.t_of(s))
+            self.norm()
+        self.update(s, lr)
 
     def host(self, lo: int = 0, hi: int | None = None) -> dict:
         hi = self.n if hi is None else hi
@@ -128,11 +161,16 @@ class OracleWindow:
 
     def step(self, s: int, sumsq_total: float | None = None):
         O = self.O
-        rows = list(S.host_contrib(self.w, s, self.i0, self.n))
+        cb = self.w.contrib_block
+        if cb:
+            codes, scales = S.host_contrib_q8(self.w, s, self.i0, self.n)
+        else:
+            rows = list(S.host_contrib(self.w, s, self.i0, self.n))
         h = self.hyper(s)
         if self.w.max_norm > 0:
             assert sumsq_total is not None
-            gbar = O.reduce_average(rows)
+            gbar = (O.reduce_average_q8(list(codes), list(scales), cb) if cb
+                    else O.reduce_average(rows))
             coef = O.clip_coef(sumsq_total, float(np.float32(self.w.max_norm)))
             O.adam(self.master, self.m, self.v, gbar, coef, h)
             p = O.f32_to_bf16(self.master)
@@ -142,7 +180,11 @@ class OracleWindow:
             self.last = O.StepOut(p, codes, scales, O.sumsq(gbar))
         else:
             h.quant_block = self.w.quant_block
-            self.last = O.step(rows, self.master, self.m, self.v, h, threads=self.threads)
+            if cb:
+                self.last = O.step_q8(list(codes), list(scales), cb, self.master, self.m,
+                                      self.v, h, threads=self.threads)
+            else:
+                self.last = O.step(rows, self.master, self.m, self.v, h, threads=self.threads)
         return self.last
 
 
@@ -154,8 +196,13 @@ def oracle_global_sumsq(w: S.Workload, s: int, chunk: int = 1 << 23, threads: in
     total = 0.0
     for lo in range(0, w.shard_len, chunk):
         n = min(chunk, w.shard_len - lo)
-        rows = S.host_contrib(w, s, lo, n)
-        _, part = O.gbar_sumsq(list(rows), threads=threads)
+        if w.contrib_block:
+            codes, scales = S.host_contrib_q8(w, s, lo, n)
+            _, part = O.gbar_sumsq_q8(list(codes), list(scales), w.contrib_block,
+                                      threads=threads)
+        else:
+            rows = S.host_contrib(w, s, lo, n)
+            _, part = O.gbar_sumsq(list(rows), threads=threads)
         total += part
     return total
 

@@ -267,3 +267,76 @@ def test_error_paths_leave_outputs_untouched():
         assert np.array_equal(before[k].view(np.uint8), after[k].view(np.uint8)), k
     g.free()
     assert Z.zero_shard_step(h, g.rows, 1e-3, 1, g.sumsq) == Z.ZS_ESTATE
+
+
+Q8_CASES = [
+    # (n, n_d, contribution block, int8 output block, clip, spill)
+    (1, 1, 32, 0, 0.0, True),
+    (7, 3, 64, 32, 0.0, True),
+    (1000, 8, 32, 256, 0.01, True),
+    (4099, 16, 256, 512, 0.05, False),
+    (65536 + 13, 24, 128, 0, 0.0, True),
+    (100_003, 64, 256, 256, 0.0, True),
+    (20_005, 5, 512, 64, 1.0, True),
+]
+
+
+@pytest.mark.parametrize("n,nd,cb,qb,clip,spill", Q8_CASES)
+def test_q8_contributions_ragged(n, nd, cb, qb, clip, spill):
+    """int8 contributions (qgZ) against the oracle's dequantizing front end,
+    narrow and wide update paths, with and without clipping and spill."""
+    import torch
+
+    log(f"case q8 n={n} n_d={nd} contrib_block={cb} out_block={qb} clip={clip} spill={spill}")
+    w = _variant("7.5B-nd64-zeropp", n_d=nd, contrib_block=cb, quant_block=qb, max_norm=clip,
+                 weight_decay=0.1 if clip else 0.0)
+    g = GpuShard(w, n=n, spill=spill)
+    g.init_state()
+    ow = OracleWindow(w, 0, n)
+    for s in range(1, 4):
+        g.fill_grads(s)
+        g.step(s)
+        torch.cuda.synchronize()
+        tot = None
+        if clip:
+            codes, scales = S.host_contrib_q8(w, s, 0, n)
+            _, tot = O.gbar_sumsq_q8(list(codes), list(scales), cb)
+            assert abs(g.sumsq.item() - tot) <= P.sumsq_tolerance(n, tot)
+        o = ow.step(s, sumsq_total=tot)
+        got = g.host()
+        P.f32_close(f"step {s} master", got["master"], ow.master)
+        P.f32_close(f"step {s} m", got["m"], ow.m)
+        P.f32_close(f"step {s} v", got["v"], ow.v)
+        P.bf16_close(f"step {s} bf16", got["p"], o.p)
+        if qb:
+            diff = P.int8_exact(f"step {s} int8", got["codes"], got["scales"], o.codes, o.scales,
+                                got["p"], o.p, qb)
+            if diff.any():
+                c2, _ = O.quant_int8(got["p"], qb)
+                blk = np.repeat(diff, qb)[:n]
+                assert np.array_equal(got["codes"][blk], c2[blk])
+    g.free()
+
+
+def test_q8_error_paths():
+    import torch
+
+    w = _variant("7.5B-nd64-zeropp", n_d=4, quant_block=0)
+    g = GpuShard(w, n=4096)
+    g.init_state()
+    g.fill_grads(1)
+    torch.cuda.synchronize()
+    before = g.host()
+    h = g.shard.h
+    assert Z.zero_shard_step_q8(h, g.qrows, g.srows, 100, 1e-3, 1) == Z.ZS_EINVAL
+    bad = list(g.qrows)
+    bad[2] = g.codes_buf[2 * g.stride + 1: 2 * g.stride + 1 + g.n]
+    assert Z.zero_shard_step_q8(h, bad, g.srows, 256, 1e-3, 1) == Z.ZS_EALIGN
+    assert Z.zero_shard_step_q8(h, g.qrows, list(g.srows[:3]) + [None], 256, 1e-3, 1) == \
+        Z.ZS_EINVAL
+    assert Z.zero_shard_gnorm_q8(h, g.qrows, None, 256, g.sumsq) == Z.ZS_EINVAL
+    torch.cuda.synchronize()
+    after = g.host()
+    for k in before:
+        assert np.array_equal(before[k].view(np.uint8), after[k].view(np.uint8)), k
+    g.free()

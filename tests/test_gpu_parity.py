@@ -134,6 +134,26 @@ def test_7p5b_nd64_windows():
     g.free()
 
 
+def test_7p5b_zeropp_windows():
+    """ZeRO++ both ways at the 7.5B, N_d = 64 size: int8 contributions in
+    (qgZ, block 256), int8 weights out (qwZ, block 256)."""
+    w = S.by_name("7.5B-nd64-zeropp")
+    n = w.shard_len
+    log(f"case {w.name}: n={n} n_d={w.n_d} steps={w.steps} contrib block={w.contrib_block}")
+    g = GpuShard(w)
+    g.init_state()
+    wins = windows(n, 10, 65536, seed=5)
+    ows = [OracleWindow(w, lo, hi - lo) for lo, hi in wins]
+    for s in range(1, w.steps + 1):
+        g.fill_grads(s)
+        g.step(s)
+        for (lo, hi), ow in zip(wins, ows):
+            o = ow.step(s)
+            if s in (1, 2, 10, 25) or s == w.steps:
+                _compare(f"{w.name} step {s} [{lo},{hi})", g.host(lo, hi), o, ow, w.quant_block)
+    g.free()
+
+
 def test_13b_clip_int8_full_norm_and_windows():
     """Clipped steps need the norm of the whole averaged gradient: the oracle
     streams all 16 x 812.5M contributions through the host for each step."""
