@@ -102,6 +102,7 @@ def lib() -> ctypes.CDLL:
         L.orc_reduce_average_q8.argtypes = [_vp, _vp, _c_i32, _c_i64, _c_i32, _vp]
         L.orc_gbar_sumsq_q8.restype = _c_f64
         L.orc_gbar_sumsq_q8.argtypes = [_vp, _vp, _c_i32, _c_i64, _c_i32, _vp, _c_i32]
+        L.orc_dequant_bf16.argtypes = [_vp, _vp, _c_i32, _c_i64, _c_i32, _vp]
         L.orc_step_q8.restype = ctypes.c_int
         L.orc_step_q8.argtypes = [_vp, _vp, _c_i32, _c_i64, _c_i32, _vp, _vp, _vp, _vp, _vp,
                                   _vp, ctypes.POINTER(OrcHyper), ctypes.POINTER(_c_f64),
@@ -276,3 +277,20 @@ def step_q8(codes, scales, block: int, master: np.ndarray, m: np.ndarray, v: np.
     if rc != 0:
         raise ValueError(f"orc_step_q8 rejected its arguments (rc={rc})")
     return StepOut(p, qc, qs, s.value)
+
+
+def dequant_bf16(codes, scales, phi: int, block: int) -> np.ndarray:
+    """Full bf16 vector of phi elements from the n_d shards' int8 codes and
+    block scales (shard r = elements [r*ceil(phi/n_d), ...))."""
+    codes = [np.ascontiguousarray(c, dtype=np.int8) for c in codes]
+    scales = [np.ascontiguousarray(x, dtype=np.float32) for x in scales]
+    nd = len(codes)
+    per = -(-phi // nd)
+    for r, (c, x) in enumerate(zip(codes, scales)):
+        ln = max(0, min(per, phi - r * per))
+        assert c.size >= ln and x.size >= -(-ln // block)
+    ct = (ctypes.c_void_p * nd)(*[_ptr(c) if c.size else None for c in codes])
+    st = (ctypes.c_void_p * nd)(*[_ptr(x) if x.size else None for x in scales])
+    out = np.empty(phi, dtype=np.uint16)
+    lib().orc_dequant_bf16(ct, st, nd, int(phi), int(block), _ptr(out))
+    return out

@@ -237,6 +237,24 @@ void orc_quant_int8(const uint16_t *p, int64_t n, int32_t block,
   }
 }
 
+/* qwZ receive side.  After the all-gather each rank holds every shard's
+ * int8 codes and block scales (WIKI "후속 기법", ZeRO++ qwZ) and rebuilds
+ * the half-precision parameters for its forward pass.  Reading: dequantize
+ * to binary32 (the product code * scale rounded once; exact in binary64
+ * first), then round to the nearest bf16, ties to even. */
+void orc_dequant_bf16(const int8_t *const *codes, const float *const *scales, int32_t nd,
+                      int64_t phi, int32_t block, uint16_t *out) {
+  const int64_t per = phi / nd + (phi % nd != 0);
+  for (int32_t r = 0; r < nd; ++r) {
+    const int64_t base = int64_t(r) * per;
+    const int64_t len = base >= phi ? 0 : (phi - base < per ? phi - base : per);
+    for (int64_t j = 0; j < len; ++j) {
+      const float x = float(double(codes[r][j]) * double(scales[r][j / block]));
+      out[base + j] = orc_f32_to_bf16(x);
+    }
+  }
+}
+
 double orc_gbar_sumsq(const uint16_t *const *rows, int32_t nd, int64_t n,
                       float *gbar, int32_t threads) {
   const int64_t nchunks = (n + kChunk - 1) / kChunk;

@@ -79,6 +79,14 @@ void orc_adam(float *master, float *m, float *v, const float *gbar,
 void orc_quant_int8(const uint16_t *p, int64_t n, int32_t block,
                     int8_t *codes, float *scales);
 
+/* qwZ receive side: the all-gathered int8 shards back to the full bf16
+ * parameter vector.  Shard r (r = 0..n_d-1) holds elements
+ * [r*ceil(phi/n_d), ...) of the flat vector, codes[r] with one fp32 scale
+ * per `block` elements of the shard (blocks start at the shard's element
+ * 0), scales[r].  out[i] = bf16(binary32(code * scale)). */
+void orc_dequant_bf16(const int8_t *const *codes, const float *const *scales, int32_t n_d,
+                      int64_t phi, int32_t block, uint16_t *out);
+
 /* The whole step a1..a5 over one shard.  Chunked over `threads` host
  * threads; chunk partial sums are combined in chunk order, so the result
  * does not depend on the thread count.  sumsq_out (may be NULL) receives

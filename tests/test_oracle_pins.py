@@ -474,3 +474,72 @@ def test_q8_step_equals_step_on_exact_values():
         assert np.array_equal(x, y)
     assert np.array_equal(outs[0][3].codes, outs[1][3].codes)
     assert outs[0][3].sumsq == outs[1][3].sumsq
+
+
+# ------------------------------------------------- qwZ receive side (dequant)
+
+def test_dequant_hand_values_and_shard_geometry():
+    """Values by hand: code * scale exact in bf16 come back exactly; each
+    shard lands at r * ceil(phi / n_d) with its own block numbering."""
+    phi, nd, block = 10, 4, 2                # shards of 3, 3, 3, 1
+    codes = [np.array([1, -2, 3], np.int8), np.array([127, 0, -127], np.int8),
+             np.array([5, 6, 7], np.int8), np.array([-1], np.int8)]
+    scales = [np.array([0.5, 4.0], np.float32), np.array([1.0, 0.25], np.float32),
+              np.array([-2.0, 1.0], np.float32), np.array([3.0], np.float32)]
+    out = _bf16_to_float(O.dequant_bf16(codes, scales, phi, block))
+    assert out.tolist() == [0.5, -1.0, 12.0, 127.0, 0.0, -31.75, -10.0, -12.0, 7.0, -3.0]
+
+
+def test_dequant_roundtrips_the_quantizer():
+    """qwZ end to end on one shard: quantize a bf16 shard with the a5 rule,
+    dequantize: every element comes back within half a quantization step
+    (plus the two roundings to binary32 and bf16), the block absmax element
+    within a relative 2^-8, and zero blocks as zeros."""
+    p = S.host_bf16(256 * 20 + 77, 21, S.AUX, 0, 0, 0, 0.02)
+    p[256 * 3:256 * 4] = 0
+    codes, scales = O.quant_int8(p, 256)
+    back = _bf16_to_float(O.dequant_bf16([codes], [scales], p.size, 256)).astype(np.float64)
+    x = _bf16_to_float(p).astype(np.float64)
+    step = np.repeat(scales.astype(np.float64), 256)[:p.size]
+    assert np.all(np.abs(back - x) <= 0.5 * step + np.abs(x) * 2.0 ** -8 + 1e-30)
+    assert not back[256 * 3:256 * 4].any()
+    for b in range(0, 20):
+        blk = slice(b * 256, (b + 1) * 256)
+        i = np.argmax(np.abs(x[blk]))
+        if x[blk][i] != 0:
+            assert abs(back[blk][i] - x[blk][i]) <= abs(x[blk][i]) * 2.0 ** -8
+
+
+def test_dequant_is_two_roundings_of_the_exact_product():
+    """Scales with 24 significant bits make code * scale inexact in binary32:
+    the result is the bf16 of the binary32-rounded product (computed here
+    with exact rationals and a by-hand nearest-even), not of the exact one."""
+    rng = np.random.default_rng(9)
+    n, block = 512, 64
+    codes = rng.integers(-127, 128, size=n).astype(np.int8)
+    scales = (rng.random(n // block) + 0.5).astype(np.float32)
+    got = O.dequant_bf16([codes], [scales], n, block)
+
+    def rne(fr: Fraction, bits: int) -> Fraction:
+        if fr == 0:
+            return fr
+        sign = -1 if fr < 0 else 1
+        a = abs(fr)
+        e = 0
+        while a >= 2:
+            a /= 2
+            e += 1
+        while a < 1:
+            a *= 2
+            e -= 1
+        q = a * 2 ** (bits - 1)
+        fl = q.numerator // q.denominator
+        rem = q - fl
+        if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2):
+            fl += 1
+        return sign * Fraction(fl, 2 ** (bits - 1)) * Fraction(2) ** e
+
+    for i in range(n):
+        exact = Fraction(int(codes[i])) * Fraction(float(scales[i // block]))
+        want = float(rne(rne(exact, 24), 8))
+        assert _bf16_to_float(got[i:i + 1])[0] == want, i
