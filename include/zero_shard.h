@@ -155,6 +155,21 @@ int zero_shard_step_q8(zs_handle *h, const int8_t *const *codes, const float *co
  * ceil(shard_len / block) floats.  Errors: ZS_EINVAL, ZS_EHIP. */
 int zero_shard_quant(zs_handle *h, int32_t block);
 
+/* qwZ receive side (ZeRO++, "ZeRO (딥 러닝)" follow-ups table "후속 기법"):
+ * after the all-gather of the n_d int8 shards, rebuild the whole bf16
+ * parameter vector.  Shard r holds flat elements [r*ceil(phi/n_d), ...) of
+ * length zero_shard_len(phi, n_d, r); codes[r] is its int8[len] (8-byte
+ * aligned) and scales[r] its fp32[ceil(len / block)] (4-byte aligned), one
+ * scale per `block` elements counted from the shard's own element 0, as
+ * zero_shard_step writes them.  codes and scales are HOST arrays of n_d
+ * device pointers (entries of empty shards may be NULL).  Writes
+ * param_out[i] = bf16(binary32(code * scale)) (nearest even) for all phi
+ * elements of param_out (device, 16-byte aligned).  No handle: it reads
+ * every rank's shard.  Asynchronous on `stream` (hipStream_t, NULL = null
+ * stream).  Errors: ZS_EINVAL, ZS_EALIGN, ZS_EDEVICE, ZS_EHIP. */
+int zero_shard_dequant(const int8_t *const *codes, const float *const *scales, int32_t n_d,
+                       int64_t phi, int32_t block, zs_bf16 *param_out, void *stream);
+
 /* Wait for the handle's stream, release its scratch and the handle.
  * Passing NULL is a no-op returning ZS_OK. */
 int zero_shard_free(zs_handle *h);

@@ -71,6 +71,10 @@ _lib.zero_shard_gnorm_q8.argtypes = [_handle_p, ctypes.c_void_p, ctypes.c_void_p
 _lib.zero_shard_step_q8.restype = ctypes.c_int
 _lib.zero_shard_step_q8.argtypes = [_handle_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
                                     ctypes.c_float, ctypes.c_int64, ctypes.c_void_p]
+_lib.zero_shard_dequant.restype = ctypes.c_int
+_lib.zero_shard_dequant.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
+                                    ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p,
+                                    ctypes.c_void_p]
 _lib.zero_shard_quant.restype = ctypes.c_int
 _lib.zero_shard_quant.argtypes = [_handle_p, ctypes.c_int32]
 _lib.zero_shard_free.restype = ctypes.c_int
@@ -81,8 +85,8 @@ _lib.zero_shard_len.restype = ctypes.c_int64
 _lib.zero_shard_len.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32]
 
 EXPORTS = ("zero_shard_init", "zero_shard_gnorm", "zero_shard_step", "zero_shard_gnorm_q8",
-           "zero_shard_step_q8", "zero_shard_quant", "zero_shard_free", "zero_shard_strerror",
-           "zero_shard_len")
+           "zero_shard_step_q8", "zero_shard_quant", "zero_shard_dequant", "zero_shard_free",
+           "zero_shard_strerror", "zero_shard_len")
 
 
 class ZeroShardError(RuntimeError):
@@ -154,6 +158,18 @@ def zero_shard_step_q8(h, codes, scales, block: int, lr: float, t: int,
 
 def zero_shard_quant(h, block: int) -> int:
     return _lib.zero_shard_quant(h, int(block))
+
+
+def zero_shard_dequant(codes, scales, n_d: int, phi: int, block: int, param_out,
+                       stream=None) -> int:
+    """param_out: 16-bit tensor of phi elements; stream: a torch stream
+    (default: the current one)."""
+    if stream is None:
+        import torch
+
+        stream = torch.cuda.current_stream()
+    return _lib.zero_shard_dequant(contrib_table(codes), contrib_table(scales), int(n_d), int(phi),
+                                   int(block), _ptr(param_out), int(stream.cuda_stream))
 
 
 def zero_shard_free(h) -> int:

@@ -71,6 +71,10 @@ constexpr int kNormBlocks = ZS_NORM_BLOCKS;  // fixed grid of the norm pass
 #ifndef ZS_NT_SPILL
 #define ZS_NT_SPILL 0
 #endif
+#ifndef ZS_NT_OUT
+#define ZS_NT_OUT 1
+#endif
+constexpr bool kNtOut = ZS_NT_OUT;  // nontemporal stores for bf16 / int8 outputs
 
 // Contribution sources: row k is rank k's gradient for this shard.
 struct Bf16Rows {
@@ -145,6 +149,15 @@ struct NormArgs {
   int64_t n;
   float *gbar_out;   // store the averaged gradient iff non-null
   double *partials;  // one per block
+};
+
+struct DequantArgs {
+  const u32x2 *c[ZS_MAX_ND];  // shard r's int8 codes
+  const float *s[ZS_MAX_ND];  // shard r's block scales
+  int32_t shift;              // log2(lane-vectors per block)
+  int64_t per;                // elements per shard (the last may be shorter)
+  int64_t phi;
+  uint16_t *out;              // bf16[phi]
 };
 
 struct QuantArgs {
@@ -339,7 +352,7 @@ __device__ __forceinline__ void quant_lane(const float (&p)[kVec], int nvalid, i
     u32x2 q;
     q.x = lo;
     q.y = hi;
-    __builtin_nontemporal_store(q, reinterpret_cast<u32x2 *>(codes) + vec);
+    st<kNtOut>(q, reinterpret_cast<u32x2 *>(codes) + vec);
   } else {
 #pragma unroll
     for (int e = 0; e < kVec; ++e)
@@ -454,7 +467,7 @@ __device__ __forceinline__ void step_vec(const StepArgs<Src> &A, int64_t vec, do
       st<nt>(o[4], v4); st<nt>(o[5], v4 + 1);
       u32x4 pv;
       pv.x = pb[0]; pv.y = pb[1]; pv.z = pb[2]; pv.w = pb[3];
-      __builtin_nontemporal_store(pv, reinterpret_cast<u32x4 *>(A.pout) + vec);
+      st<kNtOut>(pv, reinterpret_cast<u32x4 *>(A.pout) + vec);
     } else if (nvalid > 0) {
 #pragma unroll
       for (int e = 0; e < kVec; ++e) {
@@ -538,7 +551,7 @@ __global__ void __launch_bounds__(kThreads) step_kernel(const StepArgs<Src> A) {
       st<nt>(o[4], v4); st<nt>(o[5], v4 + 1);
       u32x4 pv;
       pv.x = pb[0]; pv.y = pb[1]; pv.z = pb[2]; pv.w = pb[3];
-      __builtin_nontemporal_store(pv, reinterpret_cast<u32x4 *>(A.pout) + vec);
+      st<kNtOut>(pv, reinterpret_cast<u32x4 *>(A.pout) + vec);
       if constexpr (QL > 0) quant_lane<QL>(p, kVec, vec, A.codes, A.scales);
     }
   }
@@ -663,6 +676,119 @@ __global__ void __launch_bounds__(kThreads) quant_kernel(const QuantArgs A) {
   }
 }
 
+#ifndef ZS_DQ_UNROLL
+#define ZS_DQ_UNROLL 1
+#endif
+#ifndef ZS_DQ_BLOCKS
+#define ZS_DQ_BLOCKS 4194304
+#endif
+constexpr int kDqUnroll = ZS_DQ_UNROLL;  // lane-vectors per lane per wave sweep
+constexpr int kDqBlocks = ZS_DQ_BLOCKS;  // workgroups over all shards (at most)
+
+// Dequantize one lane-vector: 8 codes times the block's scale, each product
+// a correctly rounded binary32 multiply (the exact product rounded once),
+// then 4 v_cvt_pk_bf16_f32.
+__device__ __forceinline__ u32x4 dequant_vec(u32x2 c, float sc) {
+  float x[kVec];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    x[e] = static_cast<float>(static_cast<int8_t>(c.x >> (8 * e))) * sc;
+    x[e + 4] = static_cast<float>(static_cast<int8_t>(c.y >> (8 * e))) * sc;
+  }
+  u32x4 pv;
+  pv.x = pack_bf16(x[0], x[1]);
+  pv.y = pack_bf16(x[2], x[3]);
+  pv.z = pack_bf16(x[4], x[5]);
+  pv.w = pack_bf16(x[6], x[7]);
+  return pv;
+}
+
+// Store 8 bf16 values (16 bytes) at o with the widest stores its alignment
+// allows: `align` is 16, 8, 4 or 2 bytes, uniform across the grid's shard.
+template <bool NT>
+__device__ __forceinline__ void store_bf16x8(uint16_t *o, const u32x4 v, int align) {
+  if (align >= 16) {
+    st<NT>(v, reinterpret_cast<u32x4 *>(o));
+  } else if (align == 8) {
+    u32x2 a, b;
+    a.x = v.x; a.y = v.y;
+    b.x = v.z; b.y = v.w;
+    st<NT>(a, reinterpret_cast<u32x2 *>(o));
+    st<NT>(b, reinterpret_cast<u32x2 *>(o) + 1);
+  } else if (align == 4) {
+    unsigned *w = reinterpret_cast<unsigned *>(o);
+    st<NT>(v.x, w); st<NT>(v.y, w + 1); st<NT>(v.z, w + 2); st<NT>(v.w, w + 3);
+  } else {
+    const unsigned w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int e = 0; e < kVec; ++e) o[e] = static_cast<uint16_t>(w[e / 2] >> (16 * (e & 1)));
+  }
+}
+
+// qwZ receive side: shard blockIdx.y of the all-gathered int8 shards back to
+// its slice of the bf16 parameter vector, bf16(binary32(code * scale)).
+// Lane-vectors are counted from the shard's own element 0, so code loads and
+// block scales are aligned; the slice of the output starts wherever
+// r*ceil(phi/n_d) falls, so each lane stores its 16 bytes with the widest
+// stores that alignment allows.  Each wave sweeps U*64 consecutive
+// lane-vectors per iteration (lane l takes v0+l, v0+64+l, ...); the shard's
+// last partial vector goes element by element.
+__global__ void __launch_bounds__(kThreads) dequant_kernel(const DequantArgs A) {
+  constexpr int U = kDqUnroll;
+  constexpr int64_t span = 64 * U;
+  const int r = blockIdx.y;
+  const int64_t base = int64_t(r) * A.per;
+  if (base >= A.phi) return;
+  const int64_t len = A.phi - base < A.per ? A.phi - base : A.per;
+  const int64_t off = (base * 2) & 15;  // byte offset of the slice mod 16
+  const int align = off == 0 ? 16 : (off & 7) == 0 ? 8 : (off & 3) == 0 ? 4 : 2;
+  const int64_t nvec = (len + kVec - 1) / kVec;
+  const int64_t nfull = len / kVec;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int64_t stride = int64_t(gridDim.x) * (kThreads / 64) * span;
+  uint16_t *out = A.out + base;
+  for (int64_t wb = (int64_t(blockIdx.x) * (kThreads / 64) + wave) * span; wb < nvec;
+       wb += stride) {
+    if (wb + span <= nfull) {
+      u32x2 c[U];
+      float sc[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t vec = wb + 64 * u + lane;
+        c[u] = __builtin_nontemporal_load(A.c[r] + vec);
+        sc[u] = A.s[r][vec >> A.shift];
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        store_bf16x8<kNtOut>(out + (wb + 64 * u + lane) * kVec, dequant_vec(c[u], sc[u]), align);
+      continue;
+    }
+    for (int u = 0; u < U; ++u) {
+      const int64_t vec = wb + 64 * u + lane;
+      if (vec >= nvec) break;
+      const int64_t j0 = vec * kVec;
+      const int nvalid = j0 + kVec <= len ? kVec : int(len - j0);
+      const float sc = A.s[r][vec >> A.shift];
+      if (nvalid == kVec) {
+        store_bf16x8<kNtOut>(out + j0, dequant_vec(A.c[r][vec], sc), align);
+        continue;
+      }
+      const int8_t *row = reinterpret_cast<const int8_t *>(A.c[r]) + j0;
+#pragma unroll
+      for (int e = 0; e < kVec; e += 2) {
+        if (e < nvalid) {
+          const float x0 = static_cast<float>(row[e]) * sc;
+          const float x1 = e + 1 < nvalid ? static_cast<float>(row[e + 1]) * sc : 0.0f;
+          const unsigned pb = pack_bf16(x0, x1);
+          out[j0 + e] = static_cast<uint16_t>(pb);
+          if (e + 1 < nvalid) out[j0 + e + 1] = static_cast<uint16_t>(pb >> 16);
+        }
+      }
+    }
+  }
+}
+
 // --------------------------------------------------------------- host side
 
 constexpr uint32_t kMagic = 0x5a534831u;
@@ -755,6 +881,21 @@ int current_device_ok(const zs_handle *h) {
 }
 
 int launched() { return hipGetLastError() == hipSuccess ? ZS_OK : ZS_EHIP; }
+
+// The current device is a gfx950 (checked once per device, then cached).
+int device_is_gfx950() {
+  static std::mutex mu;
+  static int state[64] = {0};  // 0 unknown, 1 gfx950, -1 other
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return ZS_EDEVICE;
+  std::lock_guard<std::mutex> lk(mu);
+  if (dev < 64 && state[dev]) return state[dev] > 0 ? ZS_OK : ZS_EDEVICE;
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return ZS_EHIP;
+  const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  if (dev < 64) state[dev] = ok ? 1 : -1;
+  return ok ? ZS_OK : ZS_EDEVICE;
+}
 
 int gnorm_args_ok(zs_handle *h, double *sumsq_dev) {
   if (!live(h)) return ZS_ESTATE;
@@ -1006,6 +1147,43 @@ int zero_shard_quant(zs_handle *h, int32_t block) {
     case 512: hipLaunchKernelGGL(quant_kernel<64>, grid, blk, 0, st, A); break;
     default: return ZS_EINVAL;
   }
+  return launched();
+}
+
+int zero_shard_dequant(const int8_t *const *codes, const float *const *scales, int32_t n_d,
+                       int64_t phi, int32_t block, zs_bf16 *param_out, void *stream) {
+  if (n_d < 1 || n_d > ZS_MAX_ND || phi < 0) return ZS_EINVAL;
+  const int lanes = quant_lanes(block);
+  if (lanes < 0) return ZS_EINVAL;
+  if (phi == 0) return ZS_OK;
+  if (!codes || !scales || !param_out) return ZS_EINVAL;
+  if (!aligned(param_out, 16)) return ZS_EALIGN;
+  DequantArgs A;
+  std::memset(&A, 0, sizeof A);
+  A.per = phi / n_d + (phi % n_d != 0);
+  A.phi = phi;
+  A.out = param_out;
+  while ((1 << A.shift) < lanes) ++A.shift;
+  int64_t longest = 0;
+  for (int r = 0; r < n_d; ++r) {
+    const int64_t len = zero_shard_len(phi, n_d, r);
+    if (len == 0) continue;
+    if (!codes[r] || !scales[r]) return ZS_EINVAL;
+    if (!aligned(codes[r], 8) || !aligned(scales[r], 4)) return ZS_EALIGN;
+    A.c[r] = reinterpret_cast<const u32x2 *>(codes[r]);
+    A.s[r] = scales[r];
+    longest = len > longest ? len : longest;
+  }
+  int rc = device_is_gfx950();
+  if (rc) return rc;
+  const int64_t nvec = (longest + kVec - 1) / kVec;
+  const int64_t per_block = int64_t(kThreads) * kDqUnroll;
+  int64_t gx = (nvec + per_block - 1) / per_block;
+  const int64_t cap = kDqBlocks / n_d > 1 ? kDqBlocks / n_d : 1;
+  if (gx > cap) gx = cap;
+  if (gx < 1) gx = 1;
+  hipLaunchKernelGGL(dequant_kernel, dim3(unsigned(gx), unsigned(n_d)), dim3(kThreads), 0,
+                     static_cast<hipStream_t>(stream), A);
   return launched();
 }
 

@@ -148,3 +148,23 @@ def test_one_hip_runtime_in_process():
     out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True,
                          check=True).stdout
     assert out.splitlines()[0] == "1", out
+
+
+@pytest.mark.parametrize("args,code", [
+    (dict(n_d=0), Z.ZS_EINVAL),
+    (dict(n_d=65), Z.ZS_EINVAL),
+    (dict(phi=-1), Z.ZS_EINVAL),
+    (dict(block=100), Z.ZS_EINVAL),
+    (dict(out=None), Z.ZS_EINVAL),
+    (dict(out=0x40002), Z.ZS_EALIGN),
+    (dict(codes=[0x1000, 0x2004, 0x3000, 0x4000]), Z.ZS_EALIGN),
+    (dict(scales=[0x1000, None, 0x3000, 0x4000]), Z.ZS_EINVAL),
+])
+def test_dequant_rejects_bad_arguments(args, code):
+    a = dict(codes=[0x1000, 0x2000, 0x3000, 0x4000], scales=[0x5000, 0x6000, 0x7000, 0x8000],
+             n_d=4, phi=1000, block=256, out=0x40000)
+    a.update(args)
+    ct = (ctypes.c_void_p * 4)(*a["codes"])
+    st = (ctypes.c_void_p * 4)(*a["scales"])
+    rc = Z._lib.zero_shard_dequant(ct, st, a["n_d"], a["phi"], a["block"], a["out"], None)
+    assert rc == code

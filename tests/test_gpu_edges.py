@@ -340,3 +340,70 @@ def test_q8_error_paths():
     for k in before:
         assert np.array_equal(before[k].view(np.uint8), after[k].view(np.uint8)), k
     g.free()
+
+
+DEQUANT_CASES = [
+    # (phi, n_d, block): uneven shards, shard bases not 16-byte aligned,
+    # empty trailing shards, every block size
+    (1, 1, 32),
+    (10, 4, 32),
+    (1001, 3, 64),
+    (3, 4, 128),
+    (100_003, 7, 256),
+    (1 << 20, 64, 512),
+    (777_777, 16, 256),
+]
+
+
+def _dequant_inputs(phi, nd, block, step=1):
+    import torch
+
+    w = _variant("7.5B-nd64-zeropp", n_d=nd, contrib_block=block)
+    per = -(-phi // nd)
+    stride = (per + 127) // 128 * 128 + 640
+    nb = -(-per // block)
+    sstride = (nb + 63) // 64 * 64 + 64
+    codes = torch.empty(nd * stride, dtype=torch.int8, device="cuda")
+    scales = torch.empty(nd * sstride, dtype=torch.float32, device="cuda")
+    S.dev_contrib_q8(w, step, codes, scales, per, stride, sstride)
+    c_h, s_h = S.host_contrib_q8(w, step, 0, per)
+    crow = [codes[r * stride: r * stride + per] for r in range(nd)]
+    srow = [scales[r * sstride: r * sstride + nb] for r in range(nd)]
+    return w, crow, srow, c_h, s_h
+
+
+@pytest.mark.parametrize("phi,nd,block", DEQUANT_CASES)
+def test_dequant_bit_exact(phi, nd, block):
+    import torch
+
+    log(f"case dequant phi={phi} n_d={nd} block={block}")
+    w, crow, srow, c_h, s_h = _dequant_inputs(phi, nd, block)
+    out = torch.full((phi + 8,), -1, dtype=torch.int16, device="cuda")
+    rc = Z.zero_shard_dequant(crow, srow, nd, phi, block, out)
+    assert rc == Z.ZS_OK
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().view(np.uint16)
+    want = O.dequant_bf16(list(c_h), list(s_h), phi, block)
+    assert np.array_equal(got[:phi], want)
+    assert (got[phi:] == 0xFFFF).all()  # nothing written past phi
+
+
+def test_dequant_roundtrips_the_fused_quantizer():
+    """The update's fused int8 output, all-gathered and dequantized, is the
+    bf16 shard within half a quantization step."""
+    import torch
+
+    w = _variant("13B-nd16-clip-int8", max_norm=0.0)
+    n = 300_000
+    g = GpuShard(w, n=n)
+    g.init_state()
+    g.fill_grads(1)
+    g.step(1)
+    out = torch.empty(n, dtype=torch.int16, device="cuda")
+    assert Z.zero_shard_dequant([g.codes], [g.scales], 1, n, w.quant_block, out) == Z.ZS_OK
+    torch.cuda.synchronize()
+    back = (out.cpu().numpy().view(np.uint16).astype(np.uint32) << 16).view(np.float32)
+    p = (g.p.cpu().numpy().view(np.uint16).astype(np.uint32) << 16).view(np.float32)
+    step = np.repeat(g.scales.cpu().numpy().astype(np.float64), w.quant_block)[:n]
+    assert np.all(np.abs(back.astype(np.float64) - p) <= 0.5 * step + np.abs(p) * 2.0 ** -8)
+    g.free()

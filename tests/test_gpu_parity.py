@@ -205,6 +205,37 @@ def test_13b_stage0_nd1_windows():
     g.free()
 
 
+def test_7p5b_dequant_full_size_windows():
+    """qwZ receive side at the 7.5B size: 64 int8 shards of 117,187,500 back
+    to a 7.5e9-element bf16 vector (15 GB); windows at shard boundaries, the
+    head and the tail against the oracle."""
+    import torch
+
+    w = S.by_name("7.5B-nd64-zeropp")
+    phi, nd, blk = w.phi, w.n_d, w.quant_block
+    per = w.shard_len
+    log(f"case dequant phi={phi} n_d={nd} block={blk}")
+    stride = (per + 127) // 128 * 128 + 640
+    nb = -(-per // blk)
+    sstride = (nb + 63) // 64 * 64 + 64
+    codes = torch.empty(nd * stride, dtype=torch.int8, device="cuda")
+    scales = torch.empty(nd * sstride, dtype=torch.float32, device="cuda")
+    S.dev_contrib_q8(w, 1, codes, scales, per, stride, sstride)
+    out = torch.empty(phi, dtype=torch.int16, device="cuda")
+    crow = [codes[r * stride: r * stride + per] for r in range(nd)]
+    srow = [scales[r * sstride: r * sstride + nb] for r in range(nd)]
+    assert Z.zero_shard_dequant(crow, srow, nd, phi, blk, out) == Z.ZS_OK
+    torch.cuda.synchronize()
+    for r in (0, 1, 31, 62, 63):
+        for j0 in (0, (per // 2) // blk * blk, per - per % blk - blk * 40):
+            ln = min(blk * 48, per - j0)
+            c_h, s_h = S.host_contrib_q8(w, 1, j0, ln)
+            want = O.dequant_bf16([c_h[r]], [s_h[r]], ln, blk)
+            got = out[r * per + j0: r * per + j0 + ln].cpu().numpy().view(np.uint16)
+            assert np.array_equal(got, want), (r, j0)
+    del out, codes, scales
+
+
 # ------------------------------------------------------------ components
 
 def test_gnorm_and_spill_match_oracle():
