@@ -103,6 +103,68 @@ def measured_traffic(w, kernel: str) -> float | None:
     return tr.get(kernel)
 
 
+def bench_dequant(w, args) -> int:
+    """qwZ receive side: phi bf16 parameters rebuilt from n_d int8 shards
+    (int8 codes + one fp32 scale per block, as the update writes them); the
+    shards are synthetic stand-ins for the all-gathered ones, resident in
+    HBM before the timed region."""
+    import torch
+
+    import seeded_inputs as S
+    import sharded_mixed_precision_zero_amd as Z
+
+    blk = w.quant_block or 256
+    phi, nd, per = w.phi, w.n_d, w.shard_len
+    w = __import__("dataclasses").replace(w, contrib_block=blk)
+    stride = (per + 127) // 128 * 128 + 640
+    nb = -(-per // blk)
+    sstride = (nb + 63) // 64 * 64 + 64
+    codes = torch.empty(nd * stride, dtype=torch.int8, device="cuda")
+    scales = torch.empty(nd * sstride, dtype=torch.float32, device="cuda")
+    S.dev_contrib_q8(w, 1, codes, scales, per, stride, sstride)
+    out = torch.empty(phi, dtype=torch.int16, device="cuda")
+    crow = [codes[r * stride: r * stride + per] for r in range(nd)]
+    srow = [scales[r * sstride: r * sstride + nb] for r in range(nd)]
+    stream = torch.cuda.current_stream()
+
+    def run():
+        rc = Z.zero_shard_dequant(crow, srow, nd, phi, blk, out)
+        if rc:
+            raise RuntimeError(Z.zero_shard_strerror(rc))
+
+    for _ in range(args.warmup):
+        run()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e in evs:
+        e[0].record(stream)
+        run()
+        e[1].record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms = sum(a.elapsed_time(b) for a, b in evs) / len(evs)
+    bpp = 1.0 + 4.0 / blk + 2.0
+    gbs = bpp * phi / (ms * 1e-3) / 1e9
+    _eprint(f"[bench] dequant {phi} params from {nd} int8 shards (block {blk}): {ms:.4f} ms, "
+            f"{gbs:.1f} GB/s ({100 * gbs / HBM_PEAK_GBS:.1f}% of 8 TB/s)")
+    line = {
+        "metric": "bf16 params rebuilt/sec and achieved HBM GB/s (qwZ receive side)",
+        "value": phi / (elapsed / args.steps), "unit": "params/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": elapsed * 1e3 / args.steps, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"{w.name} qwZ receive side", "phi": phi, "n_d": nd,
+                   "block": blk},
+        "roofline": {"bound": "hbm", "kernel": "dequant_kernel", "achieved": round(gbs, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "traffic": None},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -113,6 +175,9 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-spill", action="store_true",
                     help="clipped steps re-read the contributions instead of the fp32 spill")
+    ap.add_argument("--dequant", action="store_true",
+                    help="time the qwZ receive side instead: all n_d int8 shards of the "
+                         "workload back to the full bf16 parameter vector")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run torch copies of MIB MiB (for HBM counter scaling)")
     args = ap.parse_args()
@@ -143,6 +208,8 @@ def main() -> int:
     from tests._gpu import GpuShard
 
     w = S.by_name(args.config)
+    if args.dequant:
+        return bench_dequant(w, args)
     spill = not args.no_spill
     n = w.shard_len
     _eprint(f"[bench] workload {w.name}: shard {n} of phi {w.phi}, n_d {w.n_d}, "
