@@ -165,6 +165,76 @@ def bench_dequant(w, args) -> int:
     return 0
 
 
+def bench_offload(w, args) -> int:
+    """ZeRO-Offload step: the norm pass on the GPU leaves the averaged
+    gradient in HBM, it is downloaded to pinned host memory, the update runs
+    on host threads over host-resident fp32 state (zero_shard_host_step) and
+    the bf16 copy is uploaded; with the one-step delayed update the host
+    update of step s overlaps the GPU work of step s+1."""
+    import torch
+
+    from tests._gpu import OffloadShard
+
+    if w.contrib_block:
+        _eprint("[bench] --offload takes bf16 contributions; this workload's are int8")
+        return 2
+    threads = min(16, len(os.sched_getaffinity(0)))
+    _eprint(f"[bench] offload {w.name}: shard {w.shard_len}, host threads {threads}")
+    off = OffloadShard(w, threads=threads)
+    off.fill_grads(1)
+    torch.cuda.synchronize()
+    _eprint("[bench] offload inputs resident; warmup")
+    for s in range(1, args.warmup + 1):
+        off.step(s, delayed=True)
+    off.finish()
+    torch.cuda.synchronize()
+    off.timed = True
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        off.step(args.warmup + 1 + i, delayed=True)
+    off.finish()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    n = w.shard_len
+
+    def mean_ms(pairs):
+        return sum(a.elapsed_time(b) for a, b in pairs) / len(pairs)
+
+    norm_ms, d2h_ms, h2d_ms = mean_ms(off.ev_norm), mean_ms(off.ev_d2h), mean_ms(off.ev_h2d)
+    host_ms = 1e3 * sum(off.host_s) / len(off.host_s)
+    q = (1.0 + 4.0 / w.quant_block) if w.quant_block else 0.0
+    host_bpp = 4.0 + 24.0 + 2.0 + q
+    norm_bpp = 2.0 * w.n_d + 4.0
+    norm_gbs = norm_bpp * n / (norm_ms * 1e-3) / 1e9
+    d2h_gbs = 4.0 * n / (d2h_ms * 1e-3) / 1e9
+    h2d_gbs = 2.0 * n / (h2d_ms * 1e-3) / 1e9
+    host_gbs = host_bpp * n / (host_ms * 1e-3) / 1e9
+    _eprint(f"[bench] offload step {elapsed * 1e3 / args.steps:.2f} ms: GPU norm {norm_ms:.3f} ms "
+            f"({norm_gbs:.0f} GB/s), spill download {d2h_ms:.2f} ms ({d2h_gbs:.1f} GB/s), "
+            f"host update {host_ms:.2f} ms ({host_gbs:.1f} GB/s of host memory), "
+            f"bf16 upload {h2d_ms:.2f} ms ({h2d_gbs:.1f} GB/s)")
+    off.free()
+    line = {
+        "metric": "params updated/sec per ZeRO-Offload shard step (host Adam, one-step delay)",
+        "value": n / (elapsed / args.steps), "unit": "params/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": elapsed * 1e3 / args.steps,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f64",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name} offload", "phi": w.phi, "n_d": w.n_d,
+                   "shard_len": n, "host_threads": threads, "delayed_update": True},
+        "offload": {"gpu_norm_ms": round(norm_ms, 4), "d2h_ms": round(d2h_ms, 3),
+                    "d2h_GBps": round(d2h_gbs, 1), "host_update_ms": round(host_ms, 2),
+                    "host_bytes_per_param": host_bpp, "host_GBps": round(host_gbs, 1),
+                    "h2d_ms": round(h2d_ms, 3), "h2d_GBps": round(h2d_gbs, 1)},
+        "roofline": {"bound": "hbm", "kernel": "gnorm_partial_kernel",
+                     "achieved": round(norm_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(norm_gbs / HBM_PEAK_GBS, 4), "traffic": None},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -178,6 +248,9 @@ def main() -> int:
     ap.add_argument("--dequant", action="store_true",
                     help="time the qwZ receive side instead: all n_d int8 shards of the "
                          "workload back to the full bf16 parameter vector")
+    ap.add_argument("--offload", action="store_true",
+                    help="time the ZeRO-Offload step instead: norm pass on the GPU, update "
+                         "on host threads over host-resident state, one-step delayed")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run torch copies of MIB MiB (for HBM counter scaling)")
     args = ap.parse_args()
@@ -210,6 +283,8 @@ def main() -> int:
     w = S.by_name(args.config)
     if args.dequant:
         return bench_dequant(w, args)
+    if args.offload:
+        return bench_offload(w, args)
     spill = not args.no_spill
     n = w.shard_len
     _eprint(f"[bench] workload {w.name}: shard {n} of phi {w.phi}, n_d {w.n_d}, "

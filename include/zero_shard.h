@@ -99,8 +99,11 @@ typedef struct zs_desc {
   int32_t quant_block; /* 0: no int8; else 32, 64, 128, 256 or 512: the
                           step also writes codes and scales (fused)        */
   /* state and outputs (device pointers, caller-owned) */
-  float *master, *m, *v; /* fp32[shard_len], updated in place              */
-  zs_bf16 *param_out;    /* bf16[shard_len]                                */
+  float *master, *m, *v; /* fp32[shard_len], updated in place; these four  */
+  zs_bf16 *param_out;    /* bf16[shard_len]  may all be NULL for a norm-only
+                            handle (state offloaded to the host, see
+                            zero_shard_host_step), which needs gbar_ws and
+                            refuses zero_shard_step / zero_shard_quant     */
   int8_t *q_codes;       /* int8[shard_len]; needed iff quant_block > 0 or
                             zero_shard_quant is called                     */
   float *q_scales;       /* fp32[ceil(shard_len / block)], same condition  */
@@ -169,6 +172,20 @@ int zero_shard_quant(zs_handle *h, int32_t block);
  * stream).  Errors: ZS_EINVAL, ZS_EALIGN, ZS_EDEVICE, ZS_EHIP. */
 int zero_shard_dequant(const int8_t *const *codes, const float *const *scales, int32_t n_d,
                        int64_t phi, int32_t block, zs_bf16 *param_out, void *stream);
+
+/* ZeRO-Offload host step ("ZeRO (딥 러닝)", follow-ups table "후속 기법":
+ * optimizer states and the update in CPU memory, an optimized CPU Adam, a
+ * one-step delayed update).  a3 + a4 (+ a5) on the CPU for the shard
+ * described by d, whose master/m/v/param_out/q_codes/q_scales are HOST
+ * pointers here (d->stream and d->gbar_ws are ignored); gbar is the host
+ * fp32[shard_len] averaged gradient, e.g. the device spill that
+ * zero_shard_gnorm wrote, copied to the host.  global_sumsq is S, used iff
+ * d->max_norm > 0.  The arithmetic is the device step's, so the result is
+ * bit-identical to zero_shard_step on the same inputs.  Synchronous; runs
+ * on `threads` host threads (>= 1) over contiguous, block-aligned ranges.
+ * Errors: ZS_EINVAL. */
+int zero_shard_host_step(const zs_desc *d, const float *gbar, float lr, int64_t t,
+                         double global_sumsq, int32_t threads);
 
 /* Wait for the handle's stream, release its scratch and the handle.
  * Passing NULL is a no-op returning ZS_OK. */

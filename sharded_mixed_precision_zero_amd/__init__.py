@@ -75,6 +75,9 @@ _lib.zero_shard_dequant.restype = ctypes.c_int
 _lib.zero_shard_dequant.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
                                     ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p,
                                     ctypes.c_void_p]
+_lib.zero_shard_host_step.restype = ctypes.c_int
+_lib.zero_shard_host_step.argtypes = [ctypes.POINTER(zs_desc), ctypes.c_void_p, ctypes.c_float,
+                                      ctypes.c_int64, ctypes.c_double, ctypes.c_int32]
 _lib.zero_shard_quant.restype = ctypes.c_int
 _lib.zero_shard_quant.argtypes = [_handle_p, ctypes.c_int32]
 _lib.zero_shard_free.restype = ctypes.c_int
@@ -85,8 +88,8 @@ _lib.zero_shard_len.restype = ctypes.c_int64
 _lib.zero_shard_len.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32]
 
 EXPORTS = ("zero_shard_init", "zero_shard_gnorm", "zero_shard_step", "zero_shard_gnorm_q8",
-           "zero_shard_step_q8", "zero_shard_quant", "zero_shard_dequant", "zero_shard_free",
-           "zero_shard_strerror", "zero_shard_len")
+           "zero_shard_step_q8", "zero_shard_quant", "zero_shard_dequant",
+           "zero_shard_host_step", "zero_shard_free", "zero_shard_strerror", "zero_shard_len")
 
 
 class ZeroShardError(RuntimeError):
@@ -170,6 +173,33 @@ def zero_shard_dequant(codes, scales, n_d: int, phi: int, block: int, param_out,
         stream = torch.cuda.current_stream()
     return _lib.zero_shard_dequant(contrib_table(codes), contrib_table(scales), int(n_d), int(phi),
                                    int(block), _ptr(param_out), int(stream.cuda_stream))
+
+
+def zero_shard_host_step(desc: zs_desc, gbar_host_ptr: int, lr: float, t: int,
+                         global_sumsq: float = 0.0, threads: int = 1) -> int:
+    """desc carries HOST pointers; gbar_host_ptr: address of fp32[shard_len]
+    in host memory."""
+    return _lib.zero_shard_host_step(ctypes.byref(desc), gbar_host_ptr, float(lr), int(t),
+                                     float(global_sumsq), int(threads))
+
+
+def host_desc(*, phi: int, n_d: int, r: int, shard_len: int, master, m, v, param_out,
+              beta1: float = 0.9, beta2: float = 0.999, eps: float = 1e-8,
+              weight_decay: float = 0.0, bias_correction: bool = True, max_norm: float = 0.0,
+              quant_block: int = 0, q_codes=None, q_scales=None) -> zs_desc:
+    """A descriptor over host arrays (numpy arrays or CPU tensors) for
+    zero_shard_host_step; keep the arrays alive while it is used."""
+    def addr(a):
+        if a is None:
+            return None
+        return int(a.ctypes.data) if hasattr(a, "ctypes") else int(a.data_ptr())
+
+    return zs_desc(phi=int(phi), n_d=int(n_d), r=int(r), shard_len=int(shard_len),
+                   beta1=beta1, beta2=beta2, eps=eps, weight_decay=weight_decay,
+                   bias_correction=int(bool(bias_correction)), max_norm=max_norm,
+                   quant_block=int(quant_block), master=addr(master), m=addr(m), v=addr(v),
+                   param_out=addr(param_out), q_codes=addr(q_codes), q_scales=addr(q_scales),
+                   gbar_ws=None, stream=None)
 
 
 def zero_shard_free(h) -> int:

@@ -833,9 +833,8 @@ int64_t grid_blocks(const zs_handle *h, int64_t nvec, int unroll) {
   const int64_t per_block = int64_t(kThreads) * unroll;
   int64_t need = (nvec + per_block - 1) / per_block;
   if (need < 1) need = 1;
-  int64_t per_cu = ZS_BLOCKS_PER_CU;
-  if (const char *e = std::getenv("ZS_BLOCKS_PER_CU")) per_cu = std::atoll(e);
-  if (per_cu <= 0) return need > 0x7fffffff ? 0x7fffffff : need;  // one lane-vector per lane
+  const int64_t per_cu = ZS_BLOCKS_PER_CU;
+  if (per_cu <= 0) return need > 0x7fffffff ? 0x7fffffff : need;  // one-shot grid
   const int64_t cap = int64_t(h->cus) * per_cu;
   return need < cap ? need : cap;
 }
@@ -937,6 +936,7 @@ int step_args_ok(zs_handle *h, float lr, int64_t t, const double *global_sumsq_d
                  bool *use_spill) {
   if (!live(h)) return ZS_ESTATE;
   const zs_desc &d = h->d;
+  if (d.shard_len > 0 && !d.master) return ZS_EINVAL;  // norm-only handle
   if (!(lr >= 0.0f) || !is_finite(lr) || t < 1) return ZS_EINVAL;
   const bool clip = d.max_norm > 0.0f;
   if (clip && !global_sumsq_dev) return ZS_EINVAL;
@@ -1046,7 +1046,11 @@ int zero_shard_init(const zs_desc *d, zs_handle **out) {
   if (d->quant_block != 0 && quant_lanes(d->quant_block) < 0) return ZS_EINVAL;
   const int64_t n = d->shard_len;
   if (n > 0) {
-    if (!d->master || !d->m || !d->v || !d->param_out) return ZS_EINVAL;
+    // state and output: all four, or none (a norm-only handle, e.g. for an
+    // offloaded update whose state lives in host memory)
+    const int given = !!d->master + !!d->m + !!d->v + !!d->param_out;
+    if (given != 0 && given != 4) return ZS_EINVAL;
+    if (given == 0 && !d->gbar_ws) return ZS_EINVAL;
     if (!aligned(d->master, 16) || !aligned(d->m, 16) || !aligned(d->v, 16) ||
         !aligned(d->param_out, 16))
       return ZS_EALIGN;
@@ -1129,7 +1133,7 @@ int zero_shard_quant(zs_handle *h, int32_t block) {
   if (quant_lanes(block) < 0) return ZS_EINVAL;
   const int64_t n = d.shard_len;
   if (n > 0) {
-    if (!d.q_codes || !d.q_scales) return ZS_EINVAL;
+    if (!d.param_out || !d.q_codes || !d.q_scales) return ZS_EINVAL;
     if (!aligned(d.q_codes, 8) || !aligned(d.q_scales, 4)) return ZS_EALIGN;
   }
   int rc = current_device_ok(h);

@@ -1,0 +1,160 @@
+// zero_shard_host.cpp -- ZeRO-Offload host step (declared in
+// include/zero_shard.h: zero_shard_host_step).
+//
+// ZeRO-Offload keeps the optimizer states in host memory and runs the
+// update on the CPU ("ZeRO (딥 러닝)", follow-ups table "후속 기법":
+// optimizer states and the update moved to CPU memory and the CPU, with an
+// optimized CPU Adam and a one-step delayed update).  This is that CPU
+// update for one rank's shard: a3 + a4 (+ a5) from the averaged gradient
+// the GPU produced (the norm pass's fp32 spill, copied to the host), with
+// exactly the arithmetic of the GPU step -- binary64 from the binary32
+// state, each stored value rounded once, IEEE division and square root --
+// so an offloaded step and an on-device step give the same bits.
+//
+// Built with g++ -O3 -march=x86-64-v3 -ffp-contract=off -fno-math-errno:
+// the element loop vectorizes to 4-wide binary64 AVX2 (vdivpd and vsqrtpd
+// are correctly rounded, no contraction), and the shard is split over a
+// pool of host threads in contiguous, quantizer-block-aligned ranges.
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <thread>
+#include <vector>
+
+#include "zero_shard.h"
+
+namespace {
+
+struct HostConst {
+  double b1, omb1, b2, omb2, bc1, bc2, lr, decay, eps, coef;
+};
+
+// Nearest-even bf16 of a binary32 (bias-and-truncate form); NaN stays NaN.
+inline uint16_t to_bf16(float x) {
+  uint32_t u;
+  std::memcpy(&u, &x, sizeof u);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+inline float from_bf16(uint16_t b) {
+  const uint32_t u = uint32_t(b) << 16;
+  float x;
+  std::memcpy(&x, &u, sizeof x);
+  return x;
+}
+
+// a3 + a4 over elements [lo, hi): the same expression, in the same order, as
+// the device step.
+void adam_range(const float *__restrict gbar, float *__restrict th, float *__restrict mo,
+                float *__restrict va, uint16_t *__restrict p, int64_t lo, int64_t hi,
+                const HostConst &k) {
+  for (int64_t i = lo; i < hi; ++i) {
+    const double g = k.coef * static_cast<double>(gbar[i]);
+    const double m1 = k.b1 * static_cast<double>(mo[i]) + k.omb1 * g;
+    const double v1 = k.b2 * static_cast<double>(va[i]) + k.omb2 * (g * g);
+    const double mhat = m1 / k.bc1;
+    const double vhat = v1 / k.bc2;
+    const double t0 = static_cast<double>(th[i]);
+    const double t1 = t0 - k.decay * t0 - k.lr * mhat / (std::sqrt(vhat) + k.eps);
+    mo[i] = static_cast<float>(m1);
+    va[i] = static_cast<float>(v1);
+    th[i] = static_cast<float>(t1);
+  }
+  for (int64_t i = lo; i < hi; ++i) p[i] = to_bf16(th[i]);
+}
+
+inline float nanmax(float a, float b) {
+  if (a != a) return a;
+  return (b > a || b != b) ? b : a;
+}
+
+// a5 over blocks [b_lo, b_hi) of a shard of n elements.
+void quant_blocks(const uint16_t *p, int8_t *codes, float *scales, int64_t b_lo, int64_t b_hi,
+                  int64_t n, int64_t block) {
+  for (int64_t b = b_lo; b < b_hi; ++b) {
+    const int64_t lo = b * block, hi = lo + block < n ? lo + block : n;
+    float a = 0.0f;
+    for (int64_t i = lo; i < hi; ++i) a = nanmax(a, std::fabs(from_bf16(p[i])));
+    const float s = a / 127.0f;
+    scales[b] = s;
+    for (int64_t i = lo; i < hi; ++i) {
+      int q = 0;
+      if (s != 0.0f) {
+        float r = from_bf16(p[i]) / s;
+        if (std::isfinite(r)) {
+          r = std::nearbyint(r);  // default rounding mode: ties to even
+          r = r > 127.0f ? 127.0f : (r < -127.0f ? -127.0f : r);
+          q = static_cast<int>(r);
+        }
+      }
+      codes[i] = static_cast<int8_t>(q);
+    }
+  }
+}
+
+bool finite_pos(float x) { return std::isfinite(x) && x > 0.0f; }
+
+}  // namespace
+
+extern "C" int zero_shard_host_step(const zs_desc *d, const float *gbar, float lr, int64_t t,
+                                    double global_sumsq, int32_t threads) {
+  if (!d) return ZS_EINVAL;
+  if (d->n_d < 1 || d->n_d > ZS_MAX_ND || d->r < 0 || d->r >= d->n_d || d->phi < 0)
+    return ZS_EINVAL;
+  const int64_t want = zero_shard_len(d->phi, d->n_d, d->r);
+  if (!(d->shard_len == want || (d->r == 0 && d->shard_len == d->phi))) return ZS_EINVAL;
+  if (!(d->beta1 >= 0.0f && d->beta1 < 1.0f && d->beta2 >= 0.0f && d->beta2 < 1.0f))
+    return ZS_EINVAL;
+  if (!finite_pos(d->eps) || !(d->weight_decay >= 0.0f) || !std::isfinite(d->weight_decay))
+    return ZS_EINVAL;
+  if (d->bias_correction != 0 && d->bias_correction != 1) return ZS_EINVAL;
+  if (!std::isfinite(d->max_norm)) return ZS_EINVAL;
+  const int32_t qb = d->quant_block;
+  if (qb != 0 && qb != 32 && qb != 64 && qb != 128 && qb != 256 && qb != 512) return ZS_EINVAL;
+  if (!(lr >= 0.0f) || !std::isfinite(lr) || t < 1) return ZS_EINVAL;
+  const int64_t n = d->shard_len;
+  if (n == 0) return ZS_OK;
+  if (!gbar || !d->master || !d->m || !d->v || !d->param_out) return ZS_EINVAL;
+  if (qb && (!d->q_codes || !d->q_scales)) return ZS_EINVAL;
+
+  HostConst k;
+  const double b1 = d->beta1, b2 = d->beta2;
+  k.b1 = b1;
+  k.omb1 = 1.0 - b1;
+  k.b2 = b2;
+  k.omb2 = 1.0 - b2;
+  k.bc1 = d->bias_correction ? 1.0 - std::pow(b1, double(t)) : 1.0;
+  k.bc2 = d->bias_correction ? 1.0 - std::pow(b2, double(t)) : 1.0;
+  k.lr = double(lr);
+  k.decay = double(lr) * double(d->weight_decay);
+  k.eps = double(d->eps);
+  k.coef = 1.0;
+  if (d->max_norm > 0.0f) {
+    const double c = double(d->max_norm) / (std::sqrt(global_sumsq) + 1e-6);
+    k.coef = (c != c) ? c : (c < 1.0 ? c : 1.0);
+  }
+
+  // contiguous ranges, aligned to the quantizer block so that every block is
+  // quantized by the thread that produced its bf16 values
+  const int64_t align = qb ? qb : 64;
+  int64_t nt = threads < 1 ? 1 : threads;
+  const int64_t min_piece = int64_t(1) << 16;
+  if (nt > (n + min_piece - 1) / min_piece) nt = (n + min_piece - 1) / min_piece;
+  int64_t piece = (n + nt - 1) / nt;
+  piece = (piece + align - 1) / align * align;
+  auto work = [&](int64_t lo, int64_t hi) {
+    adam_range(gbar, d->master, d->m, d->v, d->param_out, lo, hi, k);
+    if (qb) quant_blocks(d->param_out, d->q_codes, d->q_scales, lo / qb, (hi + qb - 1) / qb, n, qb);
+  };
+  std::vector<std::thread> pool;
+  for (int64_t lo = piece; lo < n; lo += piece) {
+    const int64_t hi = lo + piece < n ? lo + piece : n;
+    pool.emplace_back(work, lo, hi);
+  }
+  work(0, piece < n ? piece : n);
+  for (auto &th : pool) th.join();
+  return ZS_OK;
+}

@@ -407,3 +407,38 @@ def test_dequant_roundtrips_the_fused_quantizer():
     step = np.repeat(g.scales.cpu().numpy().astype(np.float64), w.quant_block)[:n]
     assert np.all(np.abs(back.astype(np.float64) - p) <= 0.5 * step + np.abs(p) * 2.0 ** -8)
     g.free()
+
+
+@pytest.mark.parametrize("delayed", [False, True])
+def test_offload_equals_on_device_step(delayed):
+    """ZeRO-Offload (norm on the GPU, state and update on host threads, bf16
+    uploaded back), serial or with the one-step delayed update, gives the
+    same bits as the on-device step: same definition, same inputs."""
+    import torch
+
+    from tests._gpu import OffloadShard
+
+    w = _variant("13B-nd16-clip-int8", max_norm=0.05)
+    n = 300_001
+    log(f"case offload n={n} delayed={delayed}")
+    g = GpuShard(w, n=n)
+    g.init_state()
+    off = OffloadShard(w, n=n, threads=8)
+    for s in range(1, 5):
+        g.fill_grads(s)
+        off.fill_grads(s)
+        g.step(s)
+        off.step(s, delayed=delayed)
+        if not delayed:
+            torch.cuda.synchronize()
+    off.finish()
+    torch.cuda.synchronize()
+    got = g.host()
+    assert np.array_equal(got["master"].view(np.uint32), off.master.view(np.uint32))
+    assert np.array_equal(got["m"].view(np.uint32), off.m.view(np.uint32))
+    assert np.array_equal(got["v"].view(np.uint32), off.v.view(np.uint32))
+    assert np.array_equal(got["p"], off.p_dev.cpu().numpy().view(np.uint16))
+    assert np.array_equal(got["codes"], off.codes)
+    assert np.array_equal(got["scales"].view(np.uint32), off.scales.view(np.uint32))
+    off.free()
+    g.free()
