@@ -251,6 +251,11 @@ def main() -> int:
     ap.add_argument("--offload", action="store_true",
                     help="time the ZeRO-Offload step instead: norm pass on the GPU, update "
                          "on host threads over host-resident state, one-step delayed")
+    ap.add_argument("--bucket", type=float, default=0, metavar="ELEMS",
+                    help="bucketed step: gradient buckets of ELEMS elements (reduce_bucket_size, "
+                         "e.g. 5e8), i.e. ceil(ELEMS / n_d) shard elements per bucket rounded up "
+                         "to 512, each on one of --bucket-streams worker streams")
+    ap.add_argument("--bucket-streams", type=int, default=2)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run torch copies of MIB MiB (for HBM counter scaling)")
     args = ap.parse_args()
@@ -281,6 +286,9 @@ def main() -> int:
     from tests._gpu import GpuShard
 
     w = S.by_name(args.config)
+    if args.bucket and w.contrib_block:
+        _eprint("[bench] --bucket takes bf16 contributions; this workload's are int8")
+        return 2
     if args.dequant:
         return bench_dequant(w, args)
     if args.offload:
@@ -297,15 +305,35 @@ def main() -> int:
 
     stream = torch.cuda.current_stream()
     kb = kernel_bytes(w, spill)
+    bucket_len = 0
+    if args.bucket:
+        per = -(-int(args.bucket) // w.n_d)
+        bucket_len = -(-per // 512) * 512
+        _eprint(f"[bench] bucketed: {bucket_len} shard elements per bucket, "
+                f"{-(-n // bucket_len)} buckets, {args.bucket_streams} worker streams")
+
+    def norm():
+        if bucket_len:
+            g.shard.gnorm_bucketed(g.rows, bucket_len, g.sumsq, streams=args.bucket_streams)
+        else:
+            g.norm()
+
+    def update(s):
+        if bucket_len:
+            use_spill = g.clip and g.gbar_ws is not None
+            g.shard.step_bucketed(None if use_spill else g.rows, bucket_len, w.lr, w.t_of(s),
+                                  g.sumsq if g.clip else None, streams=args.bucket_streams)
+        else:
+            g.update(s)
 
     def one_step(s, ev=None):
         if g.clip:
             if ev is not None:
                 ev[0].record(stream)
-            g.norm()
+            norm()
         if ev is not None:
             ev[1].record(stream)
-        g.update(s)
+        update(s)
         if ev is not None:
             ev[2].record(stream)
 
@@ -351,7 +379,7 @@ def main() -> int:
 
     kernel_names = {"gnorm": "gnorm_partial_kernel",
                     "step": f"step_kernel<{w.quant_block // 8 if w.quant_block else 0}>"}
-    traffic = measured_traffic(w, kernel_names[dominant])
+    traffic = None if bucket_len else measured_traffic(w, kernel_names[dominant])
     line = {
         "metric": METRIC,
         "value": value,
@@ -365,9 +393,12 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "f64",
         "data": "synthetic",
-        "config": {"workload": w.name, "phi": w.phi, "n_d": w.n_d, "r": w.r, "shard_len": n,
+        "config": {"workload": w.name + (" bucketed" if bucket_len else ""), "phi": w.phi,
+                   "n_d": w.n_d, "r": w.r, "shard_len": n,
                    "max_norm": w.max_norm, "weight_decay": w.weight_decay,
                    "quant_block": w.quant_block, "grad_spill": bool(spill and w.max_norm > 0),
+                   "bucket_len": bucket_len or None,
+                   "bucket_streams": args.bucket_streams if bucket_len else None,
                    "parallelism": f"one rank of dp{w.n_d}"},
         "hbm": {"bytes_per_param": step_bpp, "GBps": round(step_gbs, 1),
                 "frac": round(step_gbs / HBM_PEAK_GBS, 4), "kernels": per_kernel},

@@ -153,6 +153,45 @@ int zero_shard_gnorm_q8(zs_handle *h, const int8_t *const *codes, const float *c
 int zero_shard_step_q8(zs_handle *h, const int8_t *const *codes, const float *const *scales,
                        int32_t block, float lr, int64_t t, const double *global_sumsq_dev);
 
+/* Bucketed step ("ZeRO (딥 러닝)", "DeepSpeed에서 쓰기": overlap_comm,
+ * contiguous_gradients, reduce_bucket_size in the configuration example;
+ * "ZeRO-R: 잔여 메모리 최적화": gradient communication through buffers of a
+ * fixed size, independent of the model).  Gradients reach the owner rank
+ * bucket by bucket, so the shard's elements [0, shard_len) are processed in
+ * buckets of bucket_len elements (bucket j: [j*bucket_len, ...), the last
+ * one shorter), each as soon as its slice of the contributions is in place,
+ * overlapping the arrival of later buckets.
+ *
+ * contrib is a HOST array of n_d device pointers to the whole shard's rows,
+ * as for zero_shard_gnorm (contiguous gradients: bucket j of row k starts at
+ * contrib[k] + j*bucket_len).  bucket_len > 0 is a multiple of 512 (every
+ * bucket starts on a vector and a quantizer-block boundary).  ready is NULL
+ * (everything in place) or a HOST array of ceil(shard_len / bucket_len)
+ * hipEvent_t, entries may be NULL: bucket j's work waits for ready[j],
+ * which the caller has recorded (e.g. on its communication stream after
+ * bucket j's reduce-scatter) before this call.  Buckets are distributed
+ * round-robin over `streams` (1..4) worker streams that the handle creates
+ * on first use (default priority) and that start after the work already
+ * queued on the handle's stream; the handle's stream waits for all of them
+ * before the call returns, so later calls on it are ordered after every
+ * bucket.  The first call, or one with more buckets than before, allocates
+ * the per-bucket scratch.
+ *
+ * zero_shard_gnorm_bucketed: a2's first sweep per bucket (spilling gbar as
+ * zero_shard_gnorm does), then S_local = the per-bucket sums added in
+ * bucket order, to *sumsq_dev.  Same result as zero_shard_gnorm up to the
+ * association of the binary64 sum.
+ * zero_shard_step_bucketed: the fused step (a1, a3, a4, a5) per bucket;
+ * each element's result is bit-identical to zero_shard_step's.  With
+ * clipping and gbar_ws it reads the spill and contrib may be NULL.
+ * Errors: as zero_shard_gnorm / zero_shard_step; ZS_EINVAL also for a bad
+ * bucket_len or streams; ZS_ENOMEM. */
+int zero_shard_gnorm_bucketed(zs_handle *h, const zs_bf16 *const *contrib, int64_t bucket_len,
+                              int32_t streams, const void *const *ready, double *sumsq_dev);
+int zero_shard_step_bucketed(zs_handle *h, const zs_bf16 *const *contrib, int64_t bucket_len,
+                             int32_t streams, const void *const *ready, float lr, int64_t t,
+                             const double *global_sumsq_dev);
+
 /* a5 as a separate pass: quantize param_out into q_codes / q_scales with
  * the given block (32, 64, 128, 256 or 512); q_scales must hold
  * ceil(shard_len / block) floats.  Errors: ZS_EINVAL, ZS_EHIP. */

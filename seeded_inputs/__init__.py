@@ -152,6 +152,8 @@ def _stream(stream) -> int | None:
         import torch
 
         return torch.cuda.current_stream().cuda_stream
+    if hasattr(stream, "cuda_stream"):  # a torch.cuda.Stream
+        return int(stream.cuda_stream)
     return int(stream)
 
 

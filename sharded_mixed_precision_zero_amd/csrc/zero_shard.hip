@@ -795,6 +795,9 @@ constexpr uint32_t kMagic = 0x5a534831u;
 
 }  // namespace
 
+constexpr int kMaxBucketStreams = 4;  // worker streams of the bucketed calls
+constexpr int64_t kBucketAlign = 512;  // bucket lengths are multiples of this
+
 struct zs_handle {
   uint32_t magic;
   zs_desc d;
@@ -802,6 +805,14 @@ struct zs_handle {
   int cus;
   double *partials;   // kNormBlocks fp64, library-owned scratch
   bool spill_valid;   // gbar_ws holds the gradient of the pending step
+  // bucketed calls, created on first use: worker streams (default
+  // priority), their norm partials, one fp64 sum per bucket, fork/join events
+  int nworkers;
+  hipStream_t workers[kMaxBucketStreams];
+  hipEvent_t ev_fork, ev_join[kMaxBucketStreams];
+  double *bucket_partials;  // kMaxBucketStreams * kNormBlocks
+  double *bucket_sums;
+  int64_t bucket_cap;
 };
 
 namespace {
@@ -846,6 +857,35 @@ Avg make_avg(int32_t nd) {
   a.nd_f = double(nd);
   a.inv_nd = 1.0 / double(nd);
   return a;
+}
+
+// A contiguous part [off, off + len) of the shard, launched on `st`; the
+// norm pass of a part uses its own partials.  The whole shard is the part
+// [0, shard_len) on the handle's stream.
+struct Part {
+  int64_t off, len;
+  hipStream_t st;
+  double *partials;
+};
+
+Part whole(const zs_handle *h) {
+  return Part{0, h->d.shard_len, static_cast<hipStream_t>(h->d.stream), h->partials};
+}
+
+// Row pointers advanced to shard element `off` (a multiple of the block of
+// any contribution scale and of the 8-element lane vector).
+Bf16Rows shifted(const Bf16Rows &s, int nd, int64_t off) {
+  Bf16Rows r = s;
+  for (int k = 0; k < nd; ++k) r.p[k] = s.p[k] + off / kVec;
+  return r;
+}
+Q8Rows shifted(const Q8Rows &s, int nd, int64_t off) {
+  Q8Rows r = s;
+  for (int k = 0; k < nd; ++k) {
+    r.c[k] = s.c[k] + off / kVec;
+    r.s[k] = s.s[k] + ((off / kVec) >> s.shift);
+  }
+  return r;
 }
 
 int check_rows(const zs_handle *h, const zs_bf16 *const *contrib, Bf16Rows *src) {
@@ -903,31 +943,37 @@ int gnorm_args_ok(zs_handle *h, double *sumsq_dev) {
   return ZS_OK;
 }
 
-// a2, first sweep, after the contributions were checked: block partials,
-// then the fixed-order final reduction into *sumsq_dev.
+// a2, first sweep over one part, after the contributions were checked:
+// block partials, then the fixed-order final reduction into *sumsq_dev.
 template <class Src>
-int run_gnorm(zs_handle *h, const Src &src, double *sumsq_dev) {
-  int rc = current_device_ok(h);
-  if (rc) return rc;
-  const int64_t n = h->d.shard_len;
-  const hipStream_t st = static_cast<hipStream_t>(h->d.stream);
+int launch_gnorm(zs_handle *h, const Src &src, const Part &part, double *sumsq_dev) {
+  const int64_t n = part.len;
+  const hipStream_t st = part.st;
   const int64_t nvec = (n + kVec - 1) / kVec;
   const int64_t per_block = int64_t(kThreads) * Tune<Src>::norm_unroll;
   int64_t blocks = (nvec + per_block - 1) / per_block;
   if (blocks > kNormBlocks) blocks = kNormBlocks;
   if (blocks < 1) blocks = 1;
   NormArgs<Src> A;
-  A.src = src;
+  A.src = n > 0 ? shifted(src, h->d.n_d, part.off) : src;
   A.avg = make_avg(h->d.n_d);
   A.n = n;
-  A.gbar_out = h->d.gbar_ws;
-  A.partials = h->partials;
+  A.gbar_out = h->d.gbar_ws ? h->d.gbar_ws + part.off : nullptr;
+  A.partials = part.partials;
   hipLaunchKernelGGL(gnorm_partial_kernel<Src>, dim3(unsigned(blocks)), dim3(kThreads), 0, st,
                      A);
-  if ((rc = launched())) return rc;
+  int rc = launched();
+  if (rc) return rc;
   hipLaunchKernelGGL(gnorm_final_kernel, dim3(1), dim3(kFinalThreads), 0, st,
-                     static_cast<const double *>(h->partials), int(blocks), sumsq_dev);
-  if ((rc = launched())) return rc;
+                     static_cast<const double *>(part.partials), int(blocks), sumsq_dev);
+  return launched();
+}
+
+template <class Src>
+int run_gnorm(zs_handle *h, const Src &src, double *sumsq_dev) {
+  int rc = current_device_ok(h);
+  if (rc) return rc;
+  if ((rc = launch_gnorm(h, src, whole(h), sumsq_dev))) return rc;
   h->spill_valid = h->d.gbar_ws != nullptr;
   return ZS_OK;
 }
@@ -946,19 +992,17 @@ int step_args_ok(zs_handle *h, float lr, int64_t t, const double *global_sumsq_d
   return ZS_OK;
 }
 
-// a1 + a2 (apply) + a3 + a4 (+ a5), after the arguments were checked.
+// a1 + a2 (apply) + a3 + a4 (+ a5) over one part, after the arguments
+// were checked.
 template <class Src>
-int run_step(zs_handle *h, const Src &src, float lr, int64_t t, const double *global_sumsq_dev,
-             bool use_spill) {
-  int rc = current_device_ok(h);
-  if (rc) return rc;
+int launch_step(zs_handle *h, const Src &src, const Part &part, float lr, int64_t t,
+                const double *global_sumsq_dev, bool use_spill) {
   const zs_desc &d = h->d;
-  h->spill_valid = false;
-  const int64_t n = d.shard_len;
+  const int64_t n = part.len, off = part.off;
   if (n == 0) return ZS_OK;
   const bool clip = d.max_norm > 0.0f;
   StepArgs<Src> A;
-  A.src = src;
+  A.src = use_spill ? src : shifted(src, d.n_d, off);
   A.avg = make_avg(d.n_d);
   const double b1 = d.beta1, b2 = d.beta2;
   A.k.b1 = b1;
@@ -973,14 +1017,14 @@ int run_step(zs_handle *h, const Src &src, float lr, int64_t t, const double *gl
   A.n = n;
   A.sumsq = clip ? global_sumsq_dev : nullptr;
   A.max_norm = double(d.max_norm);
-  A.gbar = use_spill ? d.gbar_ws : nullptr;
-  A.master = d.master;
-  A.m = d.m;
-  A.v = d.v;
-  A.pout = d.param_out;
-  A.codes = d.q_codes;
-  A.scales = d.q_scales;
-  const hipStream_t st = static_cast<hipStream_t>(d.stream);
+  A.gbar = use_spill ? d.gbar_ws + off : nullptr;
+  A.master = d.master + off;
+  A.m = d.m + off;
+  A.v = d.v + off;
+  A.pout = d.param_out + off;
+  A.codes = d.q_codes ? d.q_codes + off : nullptr;
+  A.scales = d.q_scales ? d.q_scales + off / (d.quant_block ? d.quant_block : 1) : nullptr;
+  const hipStream_t st = part.st;
   const int64_t nvec = (n + kVec - 1) / kVec;
   const bool wide = !A.gbar && d.n_d >= kWideMinRows;
   constexpr int WU = Tune<Src>::wide_unroll;
@@ -1003,6 +1047,114 @@ int run_step(zs_handle *h, const Src &src, float lr, int64_t t, const double *gl
   }
 #undef ZS_LAUNCH_STEP
   return launched();
+}
+
+template <class Src>
+int run_step(zs_handle *h, const Src &src, float lr, int64_t t, const double *global_sumsq_dev,
+             bool use_spill) {
+  int rc = current_device_ok(h);
+  if (rc) return rc;
+  h->spill_valid = false;
+  return launch_step(h, src, whole(h), lr, t, global_sumsq_dev, use_spill);
+}
+
+// ------------------------------------------------------------ bucketed calls
+
+// Fixed-order sum of the per-bucket sums: bucket 0 first.
+__global__ void __launch_bounds__(64) bucket_sum_kernel(const double *sums, int64_t nb,
+                                                        double *out) {
+  if (threadIdx.x != 0) return;
+  double s = 0.0;
+  for (int64_t j = 0; j < nb; ++j) s += sums[j];
+  *out = s;
+}
+
+int bucket_args_ok(const zs_handle *h, int64_t bucket_len, int32_t streams) {
+  if (bucket_len <= 0 || bucket_len % kBucketAlign != 0) return ZS_EINVAL;
+  if (streams < 1 || streams > kMaxBucketStreams) return ZS_EINVAL;
+  (void)h;
+  return ZS_OK;
+}
+
+int64_t bucket_count(const zs_handle *h, int64_t bucket_len) {
+  return (h->d.shard_len + bucket_len - 1) / bucket_len;
+}
+
+// Worker streams, events and scratch for `streams` workers and `nb`
+// buckets (created or grown here, before anything is launched).
+int bucket_setup(zs_handle *h, int32_t streams, int64_t nb) {
+  if (!h->ev_fork && hipEventCreateWithFlags(&h->ev_fork, hipEventDisableTiming) != hipSuccess)
+    return ZS_EHIP;
+  while (h->nworkers < streams) {
+    const int w = h->nworkers;
+    if (hipStreamCreateWithFlags(&h->workers[w], hipStreamNonBlocking) != hipSuccess)
+      return ZS_EHIP;
+    if (hipEventCreateWithFlags(&h->ev_join[w], hipEventDisableTiming) != hipSuccess) {
+      (void)hipStreamDestroy(h->workers[w]);
+      return ZS_EHIP;
+    }
+    ++h->nworkers;
+  }
+  if (!h->bucket_partials &&
+      hipMalloc(&h->bucket_partials, kMaxBucketStreams * kNormBlocks * sizeof(double)) !=
+          hipSuccess)
+    return ZS_ENOMEM;
+  if (nb > h->bucket_cap) {
+    // the old array may still be read by queued work
+    if (h->bucket_sums) {
+      if (hipStreamSynchronize(static_cast<hipStream_t>(h->d.stream)) != hipSuccess) return ZS_EHIP;
+      for (int w = 0; w < h->nworkers; ++w)
+        if (hipStreamSynchronize(h->workers[w]) != hipSuccess) return ZS_EHIP;
+      (void)hipFree(h->bucket_sums);
+      h->bucket_sums = nullptr;
+      h->bucket_cap = 0;
+    }
+    if (hipMalloc(&h->bucket_sums, nb * sizeof(double)) != hipSuccess) return ZS_ENOMEM;
+    h->bucket_cap = nb;
+  }
+  return ZS_OK;
+}
+
+// Workers 0..streams-1 start after everything queued on the handle's stream.
+int fork_workers(zs_handle *h, int32_t streams) {
+  const hipStream_t st = static_cast<hipStream_t>(h->d.stream);
+  if (hipEventRecord(h->ev_fork, st) != hipSuccess) return ZS_EHIP;
+  for (int w = 0; w < streams; ++w)
+    if (hipStreamWaitEvent(h->workers[w], h->ev_fork, 0) != hipSuccess) return ZS_EHIP;
+  return ZS_OK;
+}
+
+// The handle's stream continues after everything queued on the workers.
+int join_workers(zs_handle *h, int32_t streams) {
+  const hipStream_t st = static_cast<hipStream_t>(h->d.stream);
+  for (int w = 0; w < streams; ++w) {
+    if (hipEventRecord(h->ev_join[w], h->workers[w]) != hipSuccess) return ZS_EHIP;
+    if (hipStreamWaitEvent(st, h->ev_join[w], 0) != hipSuccess) return ZS_EHIP;
+  }
+  return ZS_OK;
+}
+
+int wait_ready(hipStream_t st, const void *const *ready, int64_t j) {
+  if (!ready || !ready[j]) return ZS_OK;
+  hipEvent_t e = static_cast<hipEvent_t>(const_cast<void *>(ready[j]));
+  return hipStreamWaitEvent(st, e, 0) == hipSuccess ? ZS_OK : ZS_EHIP;
+}
+
+int release_buckets(zs_handle *h) {
+  int rc = ZS_OK;
+  for (int w = 0; w < h->nworkers; ++w) {
+    if (hipStreamSynchronize(h->workers[w]) != hipSuccess) rc = ZS_EHIP;
+    if (hipStreamDestroy(h->workers[w]) != hipSuccess) rc = ZS_EHIP;
+    if (hipEventDestroy(h->ev_join[w]) != hipSuccess) rc = ZS_EHIP;
+  }
+  h->nworkers = 0;
+  if (h->ev_fork && hipEventDestroy(h->ev_fork) != hipSuccess) rc = ZS_EHIP;
+  h->ev_fork = nullptr;
+  if (h->bucket_partials && hipFree(h->bucket_partials) != hipSuccess) rc = ZS_EHIP;
+  if (h->bucket_sums && hipFree(h->bucket_sums) != hipSuccess) rc = ZS_EHIP;
+  h->bucket_partials = h->bucket_sums = nullptr;
+  h->bucket_cap = 0;
+  return rc;
 }
 
 }  // namespace
@@ -1191,6 +1343,64 @@ int zero_shard_dequant(const int8_t *const *codes, const float *const *scales, i
   return launched();
 }
 
+int zero_shard_gnorm_bucketed(zs_handle *h, const zs_bf16 *const *contrib, int64_t bucket_len,
+                              int32_t streams, const void *const *ready, double *sumsq_dev) {
+  Bf16Rows src;
+  std::memset(&src, 0, sizeof src);
+  int rc = gnorm_args_ok(h, sumsq_dev);
+  if (rc) return rc;
+  if ((rc = bucket_args_ok(h, bucket_len, streams))) return rc;
+  const int64_t n = h->d.shard_len;
+  if (n > 0 && (rc = check_rows(h, contrib, &src))) return rc;
+  if ((rc = current_device_ok(h))) return rc;
+  const int64_t nb = bucket_count(h, bucket_len);
+  if (nb == 0) return run_gnorm(h, src, sumsq_dev);  // empty shard: S = 0
+  if ((rc = bucket_setup(h, streams, nb))) return rc;
+  if ((rc = fork_workers(h, streams))) return rc;
+  for (int64_t j = 0; j < nb; ++j) {
+    const int w = int(j % streams);
+    if ((rc = wait_ready(h->workers[w], ready, j))) return rc;
+    const int64_t off = j * bucket_len;
+    const Part part{off, n - off < bucket_len ? n - off : bucket_len, h->workers[w],
+                    h->bucket_partials + int64_t(w) * kNormBlocks};
+    if ((rc = launch_gnorm(h, src, part, h->bucket_sums + j))) return rc;
+  }
+  if ((rc = join_workers(h, streams))) return rc;
+  hipLaunchKernelGGL(bucket_sum_kernel, dim3(1), dim3(64), 0,
+                     static_cast<hipStream_t>(h->d.stream),
+                     static_cast<const double *>(h->bucket_sums), nb, sumsq_dev);
+  if ((rc = launched())) return rc;
+  h->spill_valid = h->d.gbar_ws != nullptr;
+  return ZS_OK;
+}
+
+int zero_shard_step_bucketed(zs_handle *h, const zs_bf16 *const *contrib, int64_t bucket_len,
+                             int32_t streams, const void *const *ready, float lr, int64_t t,
+                             const double *global_sumsq_dev) {
+  Bf16Rows src;
+  std::memset(&src, 0, sizeof src);
+  bool use_spill = false;
+  int rc = step_args_ok(h, lr, t, global_sumsq_dev, &use_spill);
+  if (rc) return rc;
+  if ((rc = bucket_args_ok(h, bucket_len, streams))) return rc;
+  const int64_t n = h->d.shard_len;
+  if (n > 0 && !use_spill && (rc = check_rows(h, contrib, &src))) return rc;
+  if ((rc = current_device_ok(h))) return rc;
+  const int64_t nb = bucket_count(h, bucket_len);
+  h->spill_valid = false;
+  if (nb == 0) return ZS_OK;
+  if ((rc = bucket_setup(h, streams, 0))) return rc;
+  if ((rc = fork_workers(h, streams))) return rc;
+  for (int64_t j = 0; j < nb; ++j) {
+    const int w = int(j % streams);
+    if ((rc = wait_ready(h->workers[w], ready, j))) return rc;
+    const int64_t off = j * bucket_len;
+    const Part part{off, n - off < bucket_len ? n - off : bucket_len, h->workers[w], nullptr};
+    if ((rc = launch_step(h, src, part, lr, t, global_sumsq_dev, use_spill))) return rc;
+  }
+  return join_workers(h, streams);
+}
+
 int zero_shard_free(zs_handle *h) {
   if (!h) return ZS_OK;
   {
@@ -1200,6 +1410,7 @@ int zero_shard_free(zs_handle *h) {
   }
   int rc = ZS_OK;
   if (hipStreamSynchronize(static_cast<hipStream_t>(h->d.stream)) != hipSuccess) rc = ZS_EHIP;
+  if (release_buckets(h) != ZS_OK) rc = ZS_EHIP;
   if (hipFree(h->partials) != hipSuccess) rc = ZS_EHIP;
   h->magic = 0;
   delete h;

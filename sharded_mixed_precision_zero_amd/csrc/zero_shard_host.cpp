@@ -12,13 +12,16 @@
 // so an offloaded step and an on-device step give the same bits.
 //
 // Built with g++ -O3 -march=x86-64-v3 -ffp-contract=off -fno-math-errno:
-// the element loop vectorizes to 4-wide binary64 AVX2 (vdivpd and vsqrtpd
-// are correctly rounded, no contraction), and the shard is split over a
-// pool of host threads in contiguous, quantizer-block-aligned ranges.
+// the element loop vectorizes to binary64 AVX2, or AVX-512 where the host
+// has it (vdivpd and vsqrtpd are correctly rounded, no contraction, so both
+// give the same bits), and the shard is split over a pool of host threads
+// in contiguous, quantizer-block-aligned ranges.
 
 #include <cmath>
 #include <cstdint>
+#include <cstdlib>
 #include <cstring>
+#include <limits>
 #include <thread>
 #include <vector>
 
@@ -47,10 +50,10 @@ inline float from_bf16(uint16_t b) {
 }
 
 // a3 + a4 over elements [lo, hi): the same expression, in the same order, as
-// the device step.
-void adam_range(const float *__restrict gbar, float *__restrict th, float *__restrict mo,
-                float *__restrict va, uint16_t *__restrict p, int64_t lo, int64_t hi,
-                const HostConst &k) {
+// the device step.  Inlined into one body per instruction set below.
+__attribute__((always_inline)) inline void adam_range_body(
+    const float *__restrict gbar, float *__restrict th, float *__restrict mo,
+    float *__restrict va, uint16_t *__restrict p, int64_t lo, int64_t hi, const HostConst &k) {
   for (int64_t i = lo; i < hi; ++i) {
     const double g = k.coef * static_cast<double>(gbar[i]);
     const double m1 = k.b1 * static_cast<double>(mo[i]) + k.omb1 * g;
@@ -66,33 +69,66 @@ void adam_range(const float *__restrict gbar, float *__restrict th, float *__res
   for (int64_t i = lo; i < hi; ++i) p[i] = to_bf16(th[i]);
 }
 
-inline float nanmax(float a, float b) {
-  if (a != a) return a;
-  return (b > a || b != b) ? b : a;
-}
-
-// a5 over blocks [b_lo, b_hi) of a shard of n elements.
-void quant_blocks(const uint16_t *p, int8_t *codes, float *scales, int64_t b_lo, int64_t b_hi,
-                  int64_t n, int64_t block) {
+// a5 over blocks [b_lo, b_hi) of a shard of n elements.  The block absmax is
+// taken on the bf16 bit patterns: with the sign cleared, the order of the
+// patterns is the order of the magnitudes, any pattern above 0x7f80 is a NaN
+// (and then the scale is NaN and every code 0), 0x7f80 is infinity.
+__attribute__((always_inline)) inline void quant_blocks_body(
+    const uint16_t *__restrict p, int8_t *__restrict codes, float *__restrict scales,
+    int64_t b_lo, int64_t b_hi, int64_t n, int64_t block) {
   for (int64_t b = b_lo; b < b_hi; ++b) {
     const int64_t lo = b * block, hi = lo + block < n ? lo + block : n;
-    float a = 0.0f;
-    for (int64_t i = lo; i < hi; ++i) a = nanmax(a, std::fabs(from_bf16(p[i])));
+    uint16_t amax = 0;
+    for (int64_t i = lo; i < hi; ++i) {
+      const uint16_t a = p[i] & 0x7fffu;
+      amax = a > amax ? a : amax;
+    }
+    const float a = amax > 0x7f80u ? std::numeric_limits<float>::quiet_NaN() : from_bf16(amax);
     const float s = a / 127.0f;
     scales[b] = s;
+    if (!(s != 0.0f) || s != s) {  // zero block, or a NaN in it: all codes 0
+      for (int64_t i = lo; i < hi; ++i) codes[i] = 0;
+      continue;
+    }
     for (int64_t i = lo; i < hi; ++i) {
-      int q = 0;
-      if (s != 0.0f) {
-        float r = from_bf16(p[i]) / s;
-        if (std::isfinite(r)) {
-          r = std::nearbyint(r);  // default rounding mode: ties to even
-          r = r > 127.0f ? 127.0f : (r < -127.0f ? -127.0f : r);
-          q = static_cast<int>(r);
-        }
-      }
-      codes[i] = static_cast<int8_t>(q);
+      float r = from_bf16(p[i]) / s;
+      // |r| <= 127 (1 + 2^-24) for finite p; inf / inf is NaN and inf / s
+      // (s infinite only with an infinite element) cannot happen when s is
+      // finite -- both non-finite cases give code 0
+      r = (r - r == 0.0f) ? std::nearbyint(r) : 0.0f;  // default mode: ties to even
+      r = r > 127.0f ? 127.0f : (r < -127.0f ? -127.0f : r);
+      codes[i] = static_cast<int8_t>(static_cast<int>(r));
     }
   }
+}
+
+void adam_range_avx2(const float *gbar, float *th, float *mo, float *va, uint16_t *p, int64_t lo,
+                     int64_t hi, const HostConst &k) {
+  adam_range_body(gbar, th, mo, va, p, lo, hi, k);
+}
+void quant_blocks_avx2(const uint16_t *p, int8_t *codes, float *scales, int64_t b_lo,
+                       int64_t b_hi, int64_t n, int64_t block) {
+  quant_blocks_body(p, codes, scales, b_lo, b_hi, n, block);
+}
+
+#define ZS_AVX512 __attribute__((target("avx512f,avx512vl,avx512bw,avx512dq")))
+ZS_AVX512 void adam_range_avx512(const float *gbar, float *th, float *mo, float *va, uint16_t *p,
+                                 int64_t lo, int64_t hi, const HostConst &k) {
+  adam_range_body(gbar, th, mo, va, p, lo, hi, k);
+}
+ZS_AVX512 void quant_blocks_avx512(const uint16_t *p, int8_t *codes, float *scales, int64_t b_lo,
+                                   int64_t b_hi, int64_t n, int64_t block) {
+  quant_blocks_body(p, codes, scales, b_lo, b_hi, n, block);
+}
+
+// The 512-bit bodies where the host has them (same IEEE operations, so the
+// same bits), else the 256-bit ones.
+bool have_avx512() {
+  static const bool yes = __builtin_cpu_supports("avx512f") &&
+                          __builtin_cpu_supports("avx512vl") &&
+                          __builtin_cpu_supports("avx512bw") &&
+                          __builtin_cpu_supports("avx512dq");
+  return yes;
 }
 
 bool finite_pos(float x) { return std::isfinite(x) && x > 0.0f; }
@@ -145,9 +181,16 @@ extern "C" int zero_shard_host_step(const zs_desc *d, const float *gbar, float l
   if (nt > (n + min_piece - 1) / min_piece) nt = (n + min_piece - 1) / min_piece;
   int64_t piece = (n + nt - 1) / nt;
   piece = (piece + align - 1) / align * align;
+  const bool wide = have_avx512() && std::getenv("ZS_HOST_NO_AVX512") == nullptr;
   auto work = [&](int64_t lo, int64_t hi) {
-    adam_range(gbar, d->master, d->m, d->v, d->param_out, lo, hi, k);
-    if (qb) quant_blocks(d->param_out, d->q_codes, d->q_scales, lo / qb, (hi + qb - 1) / qb, n, qb);
+    const int64_t b_lo = qb ? lo / qb : 0, b_hi = qb ? (hi + qb - 1) / qb : 0;
+    if (wide) {
+      adam_range_avx512(gbar, d->master, d->m, d->v, d->param_out, lo, hi, k);
+      if (qb) quant_blocks_avx512(d->param_out, d->q_codes, d->q_scales, b_lo, b_hi, n, qb);
+    } else {
+      adam_range_avx2(gbar, d->master, d->m, d->v, d->param_out, lo, hi, k);
+      if (qb) quant_blocks_avx2(d->param_out, d->q_codes, d->q_scales, b_lo, b_hi, n, qb);
+    }
   };
   std::vector<std::thread> pool;
   for (int64_t lo = piece; lo < n; lo += piece) {

@@ -234,7 +234,8 @@ class OffloadShard:
     (zero_shard_host_step), the bf16 copy uploaded back for the next
     forward pass.  With `delayed`, the host update of step s overlaps the
     GPU's work for step s+1 (the one-step delayed update): two pinned
-    gradient slots, a copy stream, events between them."""
+    gradient slots and two pinned bf16 slots, a copy stream, events between
+    them."""
 
     def __init__(self, w: S.Workload, n: int | None = None, threads: int = 16):
         import threading  # noqa: F401
@@ -260,21 +261,24 @@ class OffloadShard:
                                  weight_decay=w.weight_decay, max_norm=w.max_norm,
                                  gbar_ws=self.gbar_dev)
         self.master, self.m, self.v = S.host_state(w, 0, n_)
-        self.p_host = torch.empty(n_, dtype=torch.int16, pin_memory=True)
+        # two pinned bf16 slots: the upload of step s-1 overlaps the host
+        # update of step s
+        self.p_host = [torch.empty(n_, dtype=torch.int16, pin_memory=True) for _ in range(2)]
         self.codes = np.empty(n_, np.int8) if w.quant_block else None
         self.scales = np.empty(-(-n_ // w.quant_block), np.float32) if w.quant_block else None
-        self.desc = Z.host_desc(phi=phi, n_d=self.nd, r=r, shard_len=n_, master=self.master,
-                                m=self.m, v=self.v, param_out=self.p_host, beta1=w.beta1,
-                                beta2=w.beta2, eps=w.eps, weight_decay=w.weight_decay,
-                                max_norm=w.max_norm, quant_block=w.quant_block,
-                                q_codes=self.codes, q_scales=self.scales)
+        self.desc = [Z.host_desc(phi=phi, n_d=self.nd, r=r, shard_len=n_, master=self.master,
+                                 m=self.m, v=self.v, param_out=self.p_host[k], beta1=w.beta1,
+                                 beta2=w.beta2, eps=w.eps, weight_decay=w.weight_decay,
+                                 max_norm=w.max_norm, quant_block=w.quant_block,
+                                 q_codes=self.codes, q_scales=self.scales) for k in range(2)]
         self.gbar_host = [torch.empty(n_, dtype=torch.float32, pin_memory=True) for _ in range(2)]
         self.sumsq_host = [torch.zeros(1, dtype=torch.float64, pin_memory=True) for _ in range(2)]
         self.compute = torch.cuda.current_stream()
         self.copy = torch.cuda.Stream()
         self.copied = [torch.cuda.Event() for _ in range(2)]
-        self.uploaded = torch.cuda.Event()
-        self.uploaded.record(self.copy)
+        self.uploaded = [torch.cuda.Event() for _ in range(2)]
+        for e in self.uploaded:
+            e.record(self.copy)
         self._worker = None
         # per-step timings: host update seconds, and (start, end) timing
         # events of the norm pass, the spill download and the bf16 upload
@@ -318,9 +322,9 @@ class OffloadShard:
         """Host update of step s from slot s % 2, then the bf16 upload."""
         slot = s % 2
         self.copied[slot].synchronize()
-        self.uploaded.synchronize()  # the previous upload has read p_host
+        self.uploaded[slot].synchronize()  # the upload of step s-2 has read p_host[slot]
         t0 = time.perf_counter()
-        rc = Z.zero_shard_host_step(self.desc, self.gbar_host[slot].data_ptr(), self.w.lr,
+        rc = Z.zero_shard_host_step(self.desc[slot], self.gbar_host[slot].data_ptr(), self.w.lr,
                                     self.w.t_of(s), float(self.sumsq_host[slot].item()),
                                     self.threads)
         if rc:
@@ -329,9 +333,9 @@ class OffloadShard:
             self.host_s.append(time.perf_counter() - t0)
         self._ev(self.ev_h2d, self.copy, True)
         with self.torch.cuda.stream(self.copy):
-            self.p_dev.copy_(self.p_host, non_blocking=True)
+            self.p_dev.copy_(self.p_host[slot], non_blocking=True)
         self._ev(self.ev_h2d, self.copy, False)
-        self.uploaded.record(self.copy)
+        self.uploaded[slot].record(self.copy)
 
     def step(self, s: int, delayed: bool = False) -> None:
         """Step s.  delayed: return once the GPU part is queued and the host
@@ -352,7 +356,8 @@ class OffloadShard:
         if self._worker is not None:
             self._worker.join()
             self._worker = None
-        self.uploaded.synchronize()
+        for e in self.uploaded:
+            e.synchronize()
 
     def free(self) -> None:
         self.finish()

@@ -1,0 +1,210 @@
+"""Bucketed step (zero_shard_gnorm_bucketed / zero_shard_step_bucketed):
+the shard processed bucket by bucket on several worker streams, each bucket
+waiting for its own arrival event.  Every element's update is the same
+definition as the unbucketed step, so the outputs must be bit-identical to
+zero_shard_step's given the same S; the bucketed S differs from the
+unbucketed one only in the association of a binary64 sum and is checked
+against the oracle's S within the rounding bound of that sum."""
+
+from __future__ import annotations
+
+import dataclasses
+
+import numpy as np
+import pytest
+
+import oracle as O
+import seeded_inputs as S
+import sharded_mixed_precision_zero_amd as Z
+from tests import _parity as P
+from tests._gpu import GpuShard, log
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _gpu_cleanup():
+    import torch
+
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    yield
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def _same(a: dict, b: dict) -> None:
+    for k in a:
+        x, y = a[k], b[k]
+        assert np.array_equal(x.view(np.uint8), y.view(np.uint8)), k
+
+
+def _bucket_rows(g: GpuShard, lo: int, hi: int):
+    """Bucket [lo, hi) of each contribution row (the views a caller's
+    per-bucket receive would fill)."""
+    return [g.rows_buf[k * g.stride + lo: k * g.stride + hi] for k in range(g.nd)]
+
+
+@pytest.mark.parametrize("name,n,bucket,streams,qb", [
+    ("gpt2-small-flat", 300_001, 65_536, 2, 0),     # ragged last bucket
+    ("gpt2-small-flat", 300_001, 512, 4, 256),      # many small buckets
+    ("7.5B-nd64", 100_000, 40_960, 3, 512),
+    ("tiny-zero1", 262_144, 262_144, 1, 64),        # one bucket
+    ("tiny-zero1", 1000, 1024, 2, 0),               # bucket longer than the shard
+])
+def test_bucketed_step_bitwise_equals_step(name, n, bucket, streams, qb):
+    import torch
+
+    w = dataclasses.replace(S.by_name(name), quant_block=qb)
+    log(f"case bucketed {name} n={n} bucket={bucket} streams={streams} qb={qb}")
+    a, b = GpuShard(w, n=n), GpuShard(w, n=n)
+    a.init_state()
+    b.init_state()
+    for s in range(1, 4):
+        a.fill_grads(s)
+        b.fill_grads(s)
+        a.step(s)
+        b.shard.step_bucketed(b.rows, bucket, w.lr, w.t_of(s), streams=streams)
+    torch.cuda.synchronize()
+    _same(a.host(), b.host())
+    a.free()
+    b.free()
+
+
+@pytest.mark.parametrize("bucket,streams", [(65_536, 2), (131_072, 4), (512 * 97, 1)])
+def test_bucketed_clipped_step(bucket, streams):
+    """Clipping with the spill: bucketed norm then bucketed step; S against
+    the oracle's, outputs bitwise against the unbucketed step run with the
+    same S."""
+    import torch
+
+    w = dataclasses.replace(S.by_name("13B-nd16-clip-int8"), max_norm=0.05)
+    n = 300_001
+    log(f"case bucketed clip n={n} bucket={bucket} streams={streams}")
+    a, b = GpuShard(w, n=n), GpuShard(w, n=n)
+    a.init_state()
+    b.init_state()
+    for s in range(1, 4):
+        a.fill_grads(s)
+        b.fill_grads(s)
+        b.shard.gnorm_bucketed(b.rows, bucket, b.sumsq, streams=streams)
+        a.norm()
+        torch.cuda.synchronize()
+        s_b, s_a = float(b.sumsq.item()), float(a.sumsq.item())
+        rows = list(S.host_contrib(w, s, 0, n))
+        _, s_o = O.gbar_sumsq(rows)
+        tol = P.sumsq_tolerance(n, s_o)
+        assert abs(s_b - s_o) <= tol, (s_b, s_o, tol)
+        assert abs(s_a - s_o) <= tol
+        a.sumsq.copy_(b.sumsq)  # the unbucketed step clips by the same S
+        a.update(s)
+        b.shard.step_bucketed(None, bucket, w.lr, w.t_of(s), b.sumsq, streams=streams)
+    torch.cuda.synchronize()
+    _same(a.host(), b.host())
+    a.free()
+    b.free()
+
+
+def test_bucketed_waits_for_arrival_events():
+    """Each bucket's contributions are written on a separate stream (the
+    stand-in for its reduce-scatter) and announced by an event; the bucketed
+    norm and step wait for them."""
+    import torch
+
+    w = dataclasses.replace(S.by_name("13B-nd16-clip-int8"), max_norm=0.05)
+    n, bucket = 1_000_003, 131_072
+    nb = -(-n // bucket)
+    log(f"case bucketed events n={n} buckets={nb}")
+    a, b = GpuShard(w, n=n), GpuShard(w, n=n)
+    a.init_state()
+    b.init_state()
+    comm = torch.cuda.Stream()
+    for s in range(1, 3):
+        a.fill_grads(s)
+        a.norm()
+        # the previous step's work on b's stream has read the rows before
+        # the new ones arrive
+        comm.wait_stream(torch.cuda.current_stream())
+        events = []
+        for j in range(nb):
+            lo, hi = j * bucket, min(n, (j + 1) * bucket)
+            view = b.rows_buf[lo:]
+            S.dev_contrib(w, s, view, hi - lo, b.stride, i0=lo, stream=comm)
+            e = torch.cuda.Event()
+            e.record(comm)
+            events.append(e)
+        b.shard.gnorm_bucketed(b.rows, bucket, b.sumsq, streams=2, ready=events)
+        a.sumsq.copy_(b.sumsq)
+        a.update(s)
+        b.shard.step_bucketed(None, bucket, w.lr, w.t_of(s), b.sumsq, streams=2, ready=events)
+    torch.cuda.synchronize()
+    _same(a.host(), b.host())
+    a.free()
+    b.free()
+
+
+def test_bucketed_unclipped_with_events_and_reuse():
+    """Unclipped: the fused step per bucket as each arrives; then the same
+    handle with fewer and with more buckets (scratch regrown)."""
+    import torch
+
+    w = S.by_name("gpt2-small-flat")
+    n = 500_000
+    a, b = GpuShard(w, n=n), GpuShard(w, n=n)
+    a.init_state()
+    b.init_state()
+    comm = torch.cuda.Stream()
+    for s, bucket in ((1, 100_352), (2, 250_368), (3, 25_088)):
+        log(f"case bucketed unclipped reuse step={s} bucket={bucket}")
+        a.fill_grads(s)
+        a.step(s)
+        nb = -(-n // bucket)
+        comm.wait_stream(torch.cuda.current_stream())
+        events = []
+        for j in range(nb):
+            lo, hi = j * bucket, min(n, (j + 1) * bucket)
+            S.dev_contrib(w, s, b.rows_buf[lo:], hi - lo, b.stride, i0=lo, stream=comm)
+            e = torch.cuda.Event()
+            e.record(comm)
+            events.append(e if j % 3 else None)  # NULL entries: no wait
+        if any(e is None for e in events):
+            comm.synchronize()  # buckets announced by NULL have arrived
+        b.shard.step_bucketed(b.rows, bucket, w.lr, w.t_of(s), streams=3, ready=events)
+    torch.cuda.synchronize()
+    _same(a.host(), b.host())
+    a.free()
+    b.free()
+
+
+def test_bucketed_empty_shard_and_errors():
+    import torch
+
+    w = S.by_name("tiny-zero1")
+    g = GpuShard(w, n=0, phi=3, r=3)
+    g.sumsq.fill_(7.0)
+    g.shard.gnorm_bucketed(g.rows, 512, g.sumsq)
+    g.shard.step_bucketed(g.rows, 512, 1e-3, 1)
+    torch.cuda.synchronize()
+    assert float(g.sumsq.item()) == 0.0
+    g.free()
+
+    w = dataclasses.replace(S.by_name("13B-nd16-clip-int8"), max_norm=0.05)
+    g = GpuShard(w, n=10_000)
+    g.init_state()
+    g.fill_grads(1)
+    before = g.host()
+    h = g.shard.h
+    assert Z.zero_shard_gnorm_bucketed(h, g.rows, 1000, 2, None, g.sumsq) == Z.ZS_EINVAL
+    assert Z.zero_shard_gnorm_bucketed(h, g.rows, 0, 2, None, g.sumsq) == Z.ZS_EINVAL
+    assert Z.zero_shard_gnorm_bucketed(h, g.rows, 512, 0, None, g.sumsq) == Z.ZS_EINVAL
+    assert Z.zero_shard_gnorm_bucketed(h, g.rows, 512, 5, None, g.sumsq) == Z.ZS_EINVAL
+    assert Z.zero_shard_gnorm_bucketed(h, g.rows, 512, 2, None, None) == Z.ZS_EINVAL
+    # the spill is not valid before a norm pass
+    assert Z.zero_shard_step_bucketed(h, None, 512, 2, None, 1e-3, 1, g.sumsq) == Z.ZS_ESTATE
+    assert Z.zero_shard_step_bucketed(h, g.rows, 512, 2, None, 1e-3, 1, None) == Z.ZS_EINVAL
+    bad = [r[1:] for r in g.rows]
+    assert Z.zero_shard_gnorm_bucketed(h, bad, 512, 2, None, g.sumsq) == Z.ZS_EALIGN
+    torch.cuda.synchronize()
+    _same(before, g.host())
+    g.free()
+    assert Z.zero_shard_gnorm_bucketed(h, g.rows, 512, 2, None, g.sumsq) == Z.ZS_ESTATE
