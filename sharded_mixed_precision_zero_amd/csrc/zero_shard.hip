@@ -54,12 +54,14 @@ constexpr int kRowGroup = ZS_ROW_GROUP;  // contribution rows loaded together (u
 #define ZS_NORM_ROW_GROUP 4
 #endif
 
-#ifndef ZS_NORM_BLOCKS
-#define ZS_NORM_BLOCKS 16384
+#ifndef ZS_NORM_FRONTS
+#define ZS_NORM_FRONTS 2
 #endif
-constexpr int kNormBlocks = ZS_NORM_BLOCKS;  // fixed grid of the norm pass
+// The norm pass's grid walks the shard as this many fronts at once (see
+// gnorm_partial_kernel).
+constexpr int kNormFronts = ZS_NORM_FRONTS;
 #ifndef ZS_NORM_UNROLL
-#define ZS_NORM_UNROLL 4
+#define ZS_NORM_UNROLL 8
 #endif
 
 #ifndef ZS_BLOCKS_PER_CU
@@ -574,10 +576,15 @@ __device__ __forceinline__ void store_gbar(float *out, int64_t vec, int nvalid,
 }
 
 // a2, first kernel: block partial sums of gbar^2 (binary64).  The grid is
-// fixed by n alone.  Each wave sweeps 64*U (U per contribution format) consecutive
-// lane-vectors per iteration (lane l takes v0+l, v0+64+l, ...); a lane's
-// sum runs over its vectors in sweep order, then a fixed butterfly over
-// the wave and the 4 wave sums in order.
+// fixed by n alone: one pass, each block 4 waves x one sweep of 64*U
+// (U per contribution format) consecutive lane-vectors (lane l takes
+// v0+l, v0+64+l, ...).  The blocks are laid out as kNormFronts contiguous
+// stretches of the shard taken in turn (block b works in stretch b mod
+// kNormFronts), so that the chip streams from several separated regions of
+// every row at once, which sustains more HBM bandwidth for this read-heavy
+// mix than a single front.  A lane's sum runs over its vectors in sweep
+// order, then a fixed butterfly over the wave and the 4 wave sums in
+// order; partial b belongs to block b.
 template <class Src>
 __global__ void __launch_bounds__(kThreads) gnorm_partial_kernel(const NormArgs<Src> A) {
   constexpr int U = Tune<Src>::norm_unroll;
@@ -586,10 +593,11 @@ __global__ void __launch_bounds__(kThreads) gnorm_partial_kernel(const NormArgs<
   const int wave = threadIdx.x >> 6;
   const int64_t nvec = (A.n + kVec - 1) / kVec;
   const int64_t nfull = A.n / kVec;
-  const int64_t stride = int64_t(gridDim.x) * (kThreads / 64) * span;
+  const int64_t per_front = int64_t(gridDim.x) / kNormFronts;  // grid: a multiple of it
+  const int64_t slot = int64_t(blockIdx.x % kNormFronts) * per_front + blockIdx.x / kNormFronts;
+  const int64_t wb = (slot * (kThreads / 64) + wave) * span;
   double acc = 0.0;
-  for (int64_t wb = (int64_t(blockIdx.x) * (kThreads / 64) + wave) * span; wb < nvec;
-       wb += stride) {
+  if (wb < nvec) {
     if (wb + span <= nfull) {
       float g[U][kVec];
       reduce_average_wave<U, Tune<Src>::norm_group>(A.src, A.avg, wb + lane, g);
@@ -803,14 +811,15 @@ struct zs_handle {
   zs_desc d;
   int device;
   int cus;
-  double *partials;   // kNormBlocks fp64, library-owned scratch
+  double *partials;   // norm_partials(shard_len) fp64, library-owned scratch
   bool spill_valid;   // gbar_ws holds the gradient of the pending step
   // bucketed calls, created on first use: worker streams (default
   // priority), their norm partials, one fp64 sum per bucket, fork/join events
   int nworkers;
   hipStream_t workers[kMaxBucketStreams];
   hipEvent_t ev_fork, ev_join[kMaxBucketStreams];
-  double *bucket_partials;  // kMaxBucketStreams * kNormBlocks
+  double *bucket_partials;  // kMaxBucketStreams * bucket_part_len
+  int64_t bucket_part_len;
   double *bucket_sums;
   int64_t bucket_cap;
 };
@@ -848,6 +857,23 @@ int64_t grid_blocks(const zs_handle *h, int64_t nvec, int unroll) {
   if (per_cu <= 0) return need > 0x7fffffff ? 0x7fffffff : need;  // one-shot grid
   const int64_t cap = int64_t(h->cus) * per_cu;
   return need < cap ? need : cap;
+}
+
+// Blocks of the norm pass over n elements: one per 4*64*U lane-vectors,
+// rounded up to a multiple of the front count.
+template <class Src>
+int64_t norm_blocks(int64_t n) {
+  const int64_t nvec = (n + kVec - 1) / kVec;
+  const int64_t per_block = int64_t(kThreads) * Tune<Src>::norm_unroll;
+  int64_t b = (nvec + per_block - 1) / per_block;
+  if (b < 1) b = 1;
+  return (b + kNormFronts - 1) / kNormFronts * kNormFronts;
+}
+
+// Partials a norm pass over n elements needs, for either contribution format.
+int64_t norm_partials(int64_t n) {
+  const int64_t a = norm_blocks<Bf16Rows>(n), b = norm_blocks<Q8Rows>(n);
+  return a > b ? a : b;
 }
 
 Avg make_avg(int32_t nd) {
@@ -949,11 +975,7 @@ template <class Src>
 int launch_gnorm(zs_handle *h, const Src &src, const Part &part, double *sumsq_dev) {
   const int64_t n = part.len;
   const hipStream_t st = part.st;
-  const int64_t nvec = (n + kVec - 1) / kVec;
-  const int64_t per_block = int64_t(kThreads) * Tune<Src>::norm_unroll;
-  int64_t blocks = (nvec + per_block - 1) / per_block;
-  if (blocks > kNormBlocks) blocks = kNormBlocks;
-  if (blocks < 1) blocks = 1;
+  const int64_t blocks = norm_blocks<Src>(n);
   NormArgs<Src> A;
   A.src = n > 0 ? shifted(src, h->d.n_d, part.off) : src;
   A.avg = make_avg(h->d.n_d);
@@ -1081,8 +1103,9 @@ int64_t bucket_count(const zs_handle *h, int64_t bucket_len) {
 }
 
 // Worker streams, events and scratch for `streams` workers and `nb`
-// buckets (created or grown here, before anything is launched).
-int bucket_setup(zs_handle *h, int32_t streams, int64_t nb) {
+// buckets of bucket_len elements (created or grown here, before anything
+// is launched).
+int bucket_setup(zs_handle *h, int32_t streams, int64_t nb, int64_t bucket_len) {
   if (!h->ev_fork && hipEventCreateWithFlags(&h->ev_fork, hipEventDisableTiming) != hipSuccess)
     return ZS_EHIP;
   while (h->nworkers < streams) {
@@ -1095,22 +1118,28 @@ int bucket_setup(zs_handle *h, int32_t streams, int64_t nb) {
     }
     ++h->nworkers;
   }
-  if (!h->bucket_partials &&
-      hipMalloc(&h->bucket_partials, kMaxBucketStreams * kNormBlocks * sizeof(double)) !=
-          hipSuccess)
-    return ZS_ENOMEM;
+  const int64_t part_len = norm_partials(bucket_len);
+  if (nb > h->bucket_cap || part_len > h->bucket_part_len) {
+    // the old arrays may still be in use by queued work
+    if (hipStreamSynchronize(static_cast<hipStream_t>(h->d.stream)) != hipSuccess) return ZS_EHIP;
+    for (int w = 0; w < h->nworkers; ++w)
+      if (hipStreamSynchronize(h->workers[w]) != hipSuccess) return ZS_EHIP;
+  }
   if (nb > h->bucket_cap) {
-    // the old array may still be read by queued work
-    if (h->bucket_sums) {
-      if (hipStreamSynchronize(static_cast<hipStream_t>(h->d.stream)) != hipSuccess) return ZS_EHIP;
-      for (int w = 0; w < h->nworkers; ++w)
-        if (hipStreamSynchronize(h->workers[w]) != hipSuccess) return ZS_EHIP;
-      (void)hipFree(h->bucket_sums);
-      h->bucket_sums = nullptr;
-      h->bucket_cap = 0;
-    }
+    if (h->bucket_sums) (void)hipFree(h->bucket_sums);
+    h->bucket_sums = nullptr;
+    h->bucket_cap = 0;
     if (hipMalloc(&h->bucket_sums, nb * sizeof(double)) != hipSuccess) return ZS_ENOMEM;
     h->bucket_cap = nb;
+  }
+  if (part_len > h->bucket_part_len) {
+    if (h->bucket_partials) (void)hipFree(h->bucket_partials);
+    h->bucket_partials = nullptr;
+    h->bucket_part_len = 0;
+    if (hipMalloc(&h->bucket_partials, kMaxBucketStreams * part_len * sizeof(double)) !=
+        hipSuccess)
+      return ZS_ENOMEM;
+    h->bucket_part_len = part_len;
   }
   return ZS_OK;
 }
@@ -1154,6 +1183,7 @@ int release_buckets(zs_handle *h) {
   if (h->bucket_sums && hipFree(h->bucket_sums) != hipSuccess) rc = ZS_EHIP;
   h->bucket_partials = h->bucket_sums = nullptr;
   h->bucket_cap = 0;
+  h->bucket_part_len = 0;
   return rc;
 }
 
@@ -1224,7 +1254,7 @@ int zero_shard_init(const zs_desc *d, zs_handle **out) {
   h->device = dev;
   h->cus = prop.multiProcessorCount > 0 ? prop.multiProcessorCount : 256;
   h->spill_valid = false;
-  if (hipMalloc(&h->partials, kNormBlocks * sizeof(double)) != hipSuccess) {
+  if (hipMalloc(&h->partials, norm_partials(n) * sizeof(double)) != hipSuccess) {
     delete h;
     return ZS_ENOMEM;
   }
@@ -1355,14 +1385,14 @@ int zero_shard_gnorm_bucketed(zs_handle *h, const zs_bf16 *const *contrib, int64
   if ((rc = current_device_ok(h))) return rc;
   const int64_t nb = bucket_count(h, bucket_len);
   if (nb == 0) return run_gnorm(h, src, sumsq_dev);  // empty shard: S = 0
-  if ((rc = bucket_setup(h, streams, nb))) return rc;
+  if ((rc = bucket_setup(h, streams, nb, bucket_len))) return rc;
   if ((rc = fork_workers(h, streams))) return rc;
   for (int64_t j = 0; j < nb; ++j) {
     const int w = int(j % streams);
     if ((rc = wait_ready(h->workers[w], ready, j))) return rc;
     const int64_t off = j * bucket_len;
     const Part part{off, n - off < bucket_len ? n - off : bucket_len, h->workers[w],
-                    h->bucket_partials + int64_t(w) * kNormBlocks};
+                    h->bucket_partials + int64_t(w) * h->bucket_part_len};
     if ((rc = launch_gnorm(h, src, part, h->bucket_sums + j))) return rc;
   }
   if ((rc = join_workers(h, streams))) return rc;
@@ -1389,7 +1419,7 @@ int zero_shard_step_bucketed(zs_handle *h, const zs_bf16 *const *contrib, int64_
   const int64_t nb = bucket_count(h, bucket_len);
   h->spill_valid = false;
   if (nb == 0) return ZS_OK;
-  if ((rc = bucket_setup(h, streams, 0))) return rc;
+  if ((rc = bucket_setup(h, streams, 0, 0))) return rc;
   if ((rc = fork_workers(h, streams))) return rc;
   for (int64_t j = 0; j < nb; ++j) {
     const int w = int(j % streams);
