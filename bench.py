@@ -358,7 +358,10 @@ def main() -> int:
     per_kernel = {}
     for k, ms in mean_ms.items():
         gbs = kb[k] * n / (ms * 1e-3) / 1e9
-        per_kernel[k] = {"mean_ms": round(ms, 4), "bytes_per_param": kb[k],
+        srt = sorted(dur[k])
+        per_kernel[k] = {"mean_ms": round(ms, 4), "median_ms": round(srt[len(srt) // 2], 4),
+                         "min_ms": round(srt[0], 4), "max_ms": round(srt[-1], 4),
+                         "bytes_per_param": kb[k],
                          "GBps": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4)}
         _eprint(f"[bench] {k}: {ms:.4f} ms, {kb[k]:.3f} B/param, {gbs:.1f} GB/s "
                 f"({100 * gbs / HBM_PEAK_GBS:.1f}% of 8 TB/s)")
