@@ -50,6 +50,9 @@ constexpr int kRowGroup = ZS_ROW_GROUP;  // contribution rows loaded together (u
 #ifndef ZS_WIDE_ROW_GROUP
 #define ZS_WIDE_ROW_GROUP 4
 #endif
+#ifndef ZS_WIDE_UNROLL
+#define ZS_WIDE_UNROLL 8
+#endif
 #ifndef ZS_NORM_ROW_GROUP
 #define ZS_NORM_ROW_GROUP 4
 #endif
@@ -107,7 +110,7 @@ template <class Src>
 struct Tune;
 template <>
 struct Tune<Bf16Rows> {
-  static constexpr int wide_unroll = 4, wide_group = ZS_WIDE_ROW_GROUP;
+  static constexpr int wide_unroll = ZS_WIDE_UNROLL, wide_group = ZS_WIDE_ROW_GROUP;
   static constexpr int norm_unroll = ZS_NORM_UNROLL, norm_group = ZS_NORM_ROW_GROUP;
 };
 template <>
