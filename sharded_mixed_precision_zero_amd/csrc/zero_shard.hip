@@ -74,7 +74,7 @@ constexpr int kNormFronts = ZS_NORM_FRONTS;
 #define ZS_NT_STATE 0
 #endif
 #ifndef ZS_NT_SPILL
-#define ZS_NT_SPILL 0
+#define ZS_NT_SPILL 1
 #endif
 #ifndef ZS_NT_OUT
 #define ZS_NT_OUT 1
