@@ -49,19 +49,13 @@ def kernel_bytes(w, spill: bool = True) -> dict[str, float]:
     return {"step": row * w.n_d + 24.0 + 2.0 + q}
 
 
-def cpu_baseline(w, target_s: float = 12.0, max_n: int = 1 << 27) -> dict:
-    """The oracle, as it stands, on a bounded sample of this workload: the
-    first S shard elements (S <= 2^27), stepped repeatedly on one resident
-    set of contributions (as the GPU run is) until about target_s seconds of
-    host time have passed; clipping uses the norm of the sample."""
+def _time_oracle(w, n: int, threads: int, target_s: float) -> tuple[int, float]:
+    """Steps of the oracle over the first n shard elements, repeated on one
+    resident set of contributions until about target_s seconds have passed:
+    (steps, seconds)."""
     import oracle as O
     import seeded_inputs as S
 
-    try:
-        threads = max(1, min(16, len(os.sched_getaffinity(0))))
-    except AttributeError:
-        threads = max(1, min(16, os.cpu_count() or 1))
-    n = min(w.shard_len, max_n)
     rows = list(S.host_contrib(w, 1, 0, n))
     master, m, v = S.host_state(w, 0, n)
     steps, spent = 0, 0.0
@@ -73,11 +67,32 @@ def cpu_baseline(w, target_s: float = 12.0, max_n: int = 1 << 27) -> dict:
         t0 = time.perf_counter()
         O.step(rows, master, m, v, h, threads=threads)
         spent += time.perf_counter() - t0
+    return steps, spent
+
+
+def cpu_baseline(w, target_s: float = 12.0, max_n: int = 1 << 27) -> dict:
+    """The oracle, as it stands, on a bounded sample of this workload: the
+    first S shard elements (S <= 2^27), stepped repeatedly on one resident
+    set of contributions (as the GPU run is) until about target_s seconds of
+    host time have passed, on all usable cores (at most 16); clipping uses
+    the norm of the sample.  Also the plain single-thread rate on a
+    2^22-element sample (about 4 s)."""
+    try:
+        threads = max(1, min(16, len(os.sched_getaffinity(0))))
+    except AttributeError:
+        threads = max(1, min(16, os.cpu_count() or 1))
+    n = min(w.shard_len, max_n)
+    steps, spent = _time_oracle(w, n, threads, target_s)
+    n1 = min(w.shard_len, 1 << 22)
+    steps1, spent1 = _time_oracle(w, n1, 1, target_s / 3)
     return {"value": n * steps / spent, "unit": "params/s", "cores": threads, "kind": "oracle",
             "sample": f"first {n} of {w.shard_len} shard elements of {w.name}, {steps} steps "
                       f"on resident inputs (norm over the sample), {threads} threads, "
                       f"{spent:.1f} s",
-            "seconds": round(spent, 3)}
+            "seconds": round(spent, 3),
+            "single_thread": {"value": n1 * steps1 / spent1, "unit": "params/s", "cores": 1,
+                              "sample": f"first {n1} elements, {steps1} steps, "
+                                        f"{spent1:.1f} s"}}
 
 
 def measured_traffic(w, kernel: str) -> float | None:
