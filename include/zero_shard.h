@@ -48,7 +48,9 @@
  * Layouts are flat, contiguous, element i at offset i.  fp32 and bf16
  * arrays and every contribution row must be 16-byte aligned; q_codes 8-byte
  * aligned.  The library owns only the handle and a small device scratch
- * (fp64 block partials of the norm, 128 KiB), allocated at init.
+ * (one fp64 partial of the norm per 16384 shard elements, or per 4096 with
+ * int8 contributions), allocated at init; the bucketed calls add worker
+ * streams and per-bucket scratch on first use.
  *
  * Errors: every call returns ZS_OK (0) or a negative zs_status.  Arguments
  * are validated before anything is queued: on an error nothing is launched
@@ -120,8 +122,8 @@ typedef struct zs_desc {
 int zero_shard_init(const zs_desc *d, zs_handle **out);
 
 /* a2, first sweep: this shard's sum of squares of the averaged gradient,
- * S_local = sum_i gbar_i^2 (binary64), reduced over a fixed grid in a fixed
- * order with no atomics (same inputs => same bits).  contrib is a HOST
+ * S_local = sum_i gbar_i^2 (binary64), reduced over a grid fixed by the
+ * shard length, in a fixed order, with no atomics (same inputs => same bits).  contrib is a HOST
  * array of n_d device pointers, contrib[k] = rank k's bf16 gradient for
  * this shard (shard-local index).  Writes S_local to *sumsq_dev (device,
  * one double).  With gbar_ws set, also stores gbar there for the next step.

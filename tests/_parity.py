@@ -78,15 +78,20 @@ def int8_exact(name: str, gpu_codes: np.ndarray, gpu_scales: np.ndarray, orc_cod
     return diff
 
 
-def sumsq_tolerance(n: int, s: float) -> float:
+def sumsq_tolerance(n: int, s: float, buckets: int = 1) -> float:
     """Bound on |S_gpu - S_oracle| for two binary64 sums of the same n
-    non-negative (exact) squares in different orders: recursive summation of
-    m terms errs by at most (m-1) u S (u = 2^-53).  The oracle sums 2^20-
-    element chunks, then the chunk partials; the GPU sums per lane over a
-    fixed grid of at most 2048 x 256 lanes, then wave, block and partial
-    trees (< 64 levels)."""
+    non-negative (exact) squares in different orders.  A summation tree of
+    height h (the most additions any term passes through) errs by at most
+    h u S (u = 2^-53).  The oracle sums 2^20-element chunks, then the chunk
+    partials.  The GPU sums per lane at most 64 squares (8 lane-vectors of
+    8 elements), then a 64-lane butterfly (6 levels) and the 4 wave sums;
+    the final kernel gives each of 1024 threads a strided run of the block
+    partials (one per 16384 elements, or per 4096 with int8 contributions)
+    and reduces them in a 10-level tree; the bucketed norm adds the bucket
+    sums in order."""
     u = 2.0 ** -53
     chunk = 1 << 20
     orc = min(n, chunk) + n // chunk + 1
-    gpu = n // (2048 * 256 * 8) + 8 + 64 + 2048
+    partials = n // 4096 + 2
+    gpu = 64 + 6 + 4 + partials // 1024 + 1 + 10 + buckets
     return (orc + gpu) * u * s

@@ -93,7 +93,7 @@ def test_bucketed_clipped_step(bucket, streams):
         s_b, s_a = float(b.sumsq.item()), float(a.sumsq.item())
         rows = list(S.host_contrib(w, s, 0, n))
         _, s_o = O.gbar_sumsq(rows)
-        tol = P.sumsq_tolerance(n, s_o)
+        tol = P.sumsq_tolerance(n, s_o, buckets=-(-n // bucket))
         assert abs(s_b - s_o) <= tol, (s_b, s_o, tol)
         assert abs(s_a - s_o) <= tol
         a.sumsq.copy_(b.sumsq)  # the unbucketed step clips by the same S
