@@ -301,9 +301,6 @@ def main() -> int:
     from tests._gpu import GpuShard
 
     w = S.by_name(args.config)
-    if args.bucket and w.contrib_block:
-        _eprint("[bench] --bucket takes bf16 contributions; this workload's are int8")
-        return 2
     if args.dequant:
         return bench_dequant(w, args)
     if args.offload:
@@ -328,18 +325,27 @@ def main() -> int:
                 f"{-(-n // bucket_len)} buckets, {args.bucket_streams} worker streams")
 
     def norm():
-        if bucket_len:
+        if bucket_len and g.cb:
+            g.shard.gnorm_bucketed_q8(g.qrows, g.srows, g.cb, bucket_len, g.sumsq,
+                                      streams=args.bucket_streams)
+        elif bucket_len:
             g.shard.gnorm_bucketed(g.rows, bucket_len, g.sumsq, streams=args.bucket_streams)
         else:
             g.norm()
 
     def update(s):
-        if bucket_len:
-            use_spill = g.clip and g.gbar_ws is not None
-            g.shard.step_bucketed(None if use_spill else g.rows, bucket_len, w.lr, w.t_of(s),
-                                  g.sumsq if g.clip else None, streams=args.bucket_streams)
-        else:
+        if not bucket_len:
             g.update(s)
+            return
+        use_spill = g.clip and g.gbar_ws is not None
+        ssq = g.sumsq if g.clip else None
+        if g.cb:
+            g.shard.step_bucketed_q8(None if use_spill else g.qrows,
+                                     None if use_spill else g.srows, g.cb, bucket_len, w.lr,
+                                     w.t_of(s), ssq, streams=args.bucket_streams)
+        else:
+            g.shard.step_bucketed(None if use_spill else g.rows, bucket_len, w.lr, w.t_of(s),
+                                  ssq, streams=args.bucket_streams)
 
     def one_step(s, ev=None):
         if g.clip:

@@ -194,6 +194,19 @@ int zero_shard_step_bucketed(zs_handle *h, const zs_bf16 *const *contrib, int64_
                              int32_t streams, const void *const *ready, float lr, int64_t t,
                              const double *global_sumsq_dev);
 
+/* The bucketed calls with int8 contributions (qgZ, as the _q8 calls above):
+ * codes[k] / scales[k] are rank k's whole-shard rows; bucket j of row k
+ * starts at codes[k] + j*bucket_len and scales[k] + j*bucket_len/block
+ * (bucket_len is a multiple of 512, so of every block).  Errors: as the
+ * bucketed calls and the _q8 calls. */
+int zero_shard_gnorm_bucketed_q8(zs_handle *h, const int8_t *const *codes,
+                                 const float *const *scales, int32_t block, int64_t bucket_len,
+                                 int32_t streams, const void *const *ready, double *sumsq_dev);
+int zero_shard_step_bucketed_q8(zs_handle *h, const int8_t *const *codes,
+                                const float *const *scales, int32_t block, int64_t bucket_len,
+                                int32_t streams, const void *const *ready, float lr, int64_t t,
+                                const double *global_sumsq_dev);
+
 /* a5 as a separate pass: quantize param_out into q_codes / q_scales with
  * the given block (32, 64, 128, 256 or 512); q_scales must hold
  * ceil(shard_len / block) floats.  Errors: ZS_EINVAL, ZS_EHIP. */

@@ -78,6 +78,15 @@ _lib.zero_shard_step_bucketed.restype = ctypes.c_int
 _lib.zero_shard_step_bucketed.argtypes = [_handle_p, ctypes.c_void_p, ctypes.c_int64,
                                           ctypes.c_int32, ctypes.c_void_p, ctypes.c_float,
                                           ctypes.c_int64, ctypes.c_void_p]
+_lib.zero_shard_gnorm_bucketed_q8.restype = ctypes.c_int
+_lib.zero_shard_gnorm_bucketed_q8.argtypes = [_handle_p, ctypes.c_void_p, ctypes.c_void_p,
+                                              ctypes.c_int32, ctypes.c_int64, ctypes.c_int32,
+                                              ctypes.c_void_p, ctypes.c_void_p]
+_lib.zero_shard_step_bucketed_q8.restype = ctypes.c_int
+_lib.zero_shard_step_bucketed_q8.argtypes = [_handle_p, ctypes.c_void_p, ctypes.c_void_p,
+                                             ctypes.c_int32, ctypes.c_int64, ctypes.c_int32,
+                                             ctypes.c_void_p, ctypes.c_float, ctypes.c_int64,
+                                             ctypes.c_void_p]
 _lib.zero_shard_dequant.restype = ctypes.c_int
 _lib.zero_shard_dequant.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
                                     ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p,
@@ -96,6 +105,7 @@ _lib.zero_shard_len.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32]
 
 EXPORTS = ("zero_shard_init", "zero_shard_gnorm", "zero_shard_step", "zero_shard_gnorm_q8",
            "zero_shard_step_q8", "zero_shard_gnorm_bucketed", "zero_shard_step_bucketed",
+           "zero_shard_gnorm_bucketed_q8", "zero_shard_step_bucketed_q8",
            "zero_shard_quant", "zero_shard_dequant",
            "zero_shard_host_step", "zero_shard_free", "zero_shard_strerror", "zero_shard_len")
 
@@ -189,6 +199,21 @@ def zero_shard_step_bucketed(h, contrib, bucket_len: int, streams: int, ready, l
     return _lib.zero_shard_step_bucketed(h, contrib_table(contrib), int(bucket_len),
                                          int(streams), event_table(ready), float(lr), int(t),
                                          _ptr(global_sumsq_dev))
+
+
+def zero_shard_gnorm_bucketed_q8(h, codes, scales, block: int, bucket_len: int, streams: int,
+                                 ready, sumsq_dev) -> int:
+    return _lib.zero_shard_gnorm_bucketed_q8(h, contrib_table(codes), contrib_table(scales),
+                                             int(block), int(bucket_len), int(streams),
+                                             event_table(ready), _ptr(sumsq_dev))
+
+
+def zero_shard_step_bucketed_q8(h, codes, scales, block: int, bucket_len: int, streams: int,
+                                ready, lr: float, t: int, global_sumsq_dev=None) -> int:
+    return _lib.zero_shard_step_bucketed_q8(h, contrib_table(codes), contrib_table(scales),
+                                            int(block), int(bucket_len), int(streams),
+                                            event_table(ready), float(lr), int(t),
+                                            _ptr(global_sumsq_dev))
 
 
 def zero_shard_quant(h, block: int) -> int:
@@ -291,6 +316,17 @@ class ZeroShard:
                       streams: int = 2, ready=None) -> None:
         _check(zero_shard_step_bucketed(self.h, contrib, bucket_len, streams, ready, lr, t,
                                         global_sumsq_dev), "zero_shard_step_bucketed")
+
+    def gnorm_bucketed_q8(self, codes, scales, block: int, bucket_len: int, sumsq_dev,
+                          streams: int = 2, ready=None) -> None:
+        _check(zero_shard_gnorm_bucketed_q8(self.h, codes, scales, block, bucket_len, streams,
+                                            ready, sumsq_dev), "zero_shard_gnorm_bucketed_q8")
+
+    def step_bucketed_q8(self, codes, scales, block: int, bucket_len: int, lr: float, t: int,
+                         global_sumsq_dev=None, streams: int = 2, ready=None) -> None:
+        _check(zero_shard_step_bucketed_q8(self.h, codes, scales, block, bucket_len, streams,
+                                           ready, lr, t, global_sumsq_dev),
+               "zero_shard_step_bucketed_q8")
 
     def quant(self, block: int) -> None:
         _check(zero_shard_quant(self.h, block), "zero_shard_quant")

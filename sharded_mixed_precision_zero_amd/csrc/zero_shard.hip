@@ -1190,6 +1190,59 @@ int release_buckets(zs_handle *h) {
   return rc;
 }
 
+// The bucketed norm pass after the arguments were checked: bucket j on
+// worker j mod streams once ready[j] has fired, its sum into bucket_sums[j],
+// then the sums in bucket order on the handle's stream.
+template <class Src>
+int run_gnorm_bucketed(zs_handle *h, const Src &src, int64_t bucket_len, int32_t streams,
+                       const void *const *ready, double *sumsq_dev) {
+  int rc = current_device_ok(h);
+  if (rc) return rc;
+  const int64_t n = h->d.shard_len;
+  const int64_t nb = bucket_count(h, bucket_len);
+  if (nb == 0) return run_gnorm(h, src, sumsq_dev);  // empty shard: S = 0
+  if ((rc = bucket_setup(h, streams, nb, bucket_len))) return rc;
+  if ((rc = fork_workers(h, streams))) return rc;
+  for (int64_t j = 0; j < nb; ++j) {
+    const int w = int(j % streams);
+    if ((rc = wait_ready(h->workers[w], ready, j))) return rc;
+    const int64_t off = j * bucket_len;
+    const Part part{off, n - off < bucket_len ? n - off : bucket_len, h->workers[w],
+                    h->bucket_partials + int64_t(w) * h->bucket_part_len};
+    if ((rc = launch_gnorm(h, src, part, h->bucket_sums + j))) return rc;
+  }
+  if ((rc = join_workers(h, streams))) return rc;
+  hipLaunchKernelGGL(bucket_sum_kernel, dim3(1), dim3(64), 0,
+                     static_cast<hipStream_t>(h->d.stream),
+                     static_cast<const double *>(h->bucket_sums), nb, sumsq_dev);
+  if ((rc = launched())) return rc;
+  h->spill_valid = h->d.gbar_ws != nullptr;
+  return ZS_OK;
+}
+
+// The bucketed update after the arguments were checked.
+template <class Src>
+int run_step_bucketed(zs_handle *h, const Src &src, int64_t bucket_len, int32_t streams,
+                      const void *const *ready, float lr, int64_t t,
+                      const double *global_sumsq_dev, bool use_spill) {
+  int rc = current_device_ok(h);
+  if (rc) return rc;
+  const int64_t n = h->d.shard_len;
+  const int64_t nb = bucket_count(h, bucket_len);
+  h->spill_valid = false;
+  if (nb == 0) return ZS_OK;
+  if ((rc = bucket_setup(h, streams, 0, 0))) return rc;
+  if ((rc = fork_workers(h, streams))) return rc;
+  for (int64_t j = 0; j < nb; ++j) {
+    const int w = int(j % streams);
+    if ((rc = wait_ready(h->workers[w], ready, j))) return rc;
+    const int64_t off = j * bucket_len;
+    const Part part{off, n - off < bucket_len ? n - off : bucket_len, h->workers[w], nullptr};
+    if ((rc = launch_step(h, src, part, lr, t, global_sumsq_dev, use_spill))) return rc;
+  }
+  return join_workers(h, streams);
+}
+
 }  // namespace
 
 extern "C" {
@@ -1383,28 +1436,21 @@ int zero_shard_gnorm_bucketed(zs_handle *h, const zs_bf16 *const *contrib, int64
   int rc = gnorm_args_ok(h, sumsq_dev);
   if (rc) return rc;
   if ((rc = bucket_args_ok(h, bucket_len, streams))) return rc;
-  const int64_t n = h->d.shard_len;
-  if (n > 0 && (rc = check_rows(h, contrib, &src))) return rc;
-  if ((rc = current_device_ok(h))) return rc;
-  const int64_t nb = bucket_count(h, bucket_len);
-  if (nb == 0) return run_gnorm(h, src, sumsq_dev);  // empty shard: S = 0
-  if ((rc = bucket_setup(h, streams, nb, bucket_len))) return rc;
-  if ((rc = fork_workers(h, streams))) return rc;
-  for (int64_t j = 0; j < nb; ++j) {
-    const int w = int(j % streams);
-    if ((rc = wait_ready(h->workers[w], ready, j))) return rc;
-    const int64_t off = j * bucket_len;
-    const Part part{off, n - off < bucket_len ? n - off : bucket_len, h->workers[w],
-                    h->bucket_partials + int64_t(w) * h->bucket_part_len};
-    if ((rc = launch_gnorm(h, src, part, h->bucket_sums + j))) return rc;
-  }
-  if ((rc = join_workers(h, streams))) return rc;
-  hipLaunchKernelGGL(bucket_sum_kernel, dim3(1), dim3(64), 0,
-                     static_cast<hipStream_t>(h->d.stream),
-                     static_cast<const double *>(h->bucket_sums), nb, sumsq_dev);
-  if ((rc = launched())) return rc;
-  h->spill_valid = h->d.gbar_ws != nullptr;
-  return ZS_OK;
+  if (h->d.shard_len > 0 && (rc = check_rows(h, contrib, &src))) return rc;
+  return run_gnorm_bucketed(h, src, bucket_len, streams, ready, sumsq_dev);
+}
+
+int zero_shard_gnorm_bucketed_q8(zs_handle *h, const int8_t *const *codes,
+                                 const float *const *scales, int32_t block, int64_t bucket_len,
+                                 int32_t streams, const void *const *ready, double *sumsq_dev) {
+  Q8Rows src;
+  std::memset(&src, 0, sizeof src);
+  int rc = gnorm_args_ok(h, sumsq_dev);
+  if (rc) return rc;
+  if (quant_lanes(block) < 0) return ZS_EINVAL;
+  if ((rc = bucket_args_ok(h, bucket_len, streams))) return rc;
+  if (h->d.shard_len > 0 && (rc = check_q8(h, codes, scales, block, &src))) return rc;
+  return run_gnorm_bucketed(h, src, bucket_len, streams, ready, sumsq_dev);
 }
 
 int zero_shard_step_bucketed(zs_handle *h, const zs_bf16 *const *contrib, int64_t bucket_len,
@@ -1416,22 +1462,26 @@ int zero_shard_step_bucketed(zs_handle *h, const zs_bf16 *const *contrib, int64_
   int rc = step_args_ok(h, lr, t, global_sumsq_dev, &use_spill);
   if (rc) return rc;
   if ((rc = bucket_args_ok(h, bucket_len, streams))) return rc;
-  const int64_t n = h->d.shard_len;
-  if (n > 0 && !use_spill && (rc = check_rows(h, contrib, &src))) return rc;
-  if ((rc = current_device_ok(h))) return rc;
-  const int64_t nb = bucket_count(h, bucket_len);
-  h->spill_valid = false;
-  if (nb == 0) return ZS_OK;
-  if ((rc = bucket_setup(h, streams, 0, 0))) return rc;
-  if ((rc = fork_workers(h, streams))) return rc;
-  for (int64_t j = 0; j < nb; ++j) {
-    const int w = int(j % streams);
-    if ((rc = wait_ready(h->workers[w], ready, j))) return rc;
-    const int64_t off = j * bucket_len;
-    const Part part{off, n - off < bucket_len ? n - off : bucket_len, h->workers[w], nullptr};
-    if ((rc = launch_step(h, src, part, lr, t, global_sumsq_dev, use_spill))) return rc;
-  }
-  return join_workers(h, streams);
+  if (h->d.shard_len > 0 && !use_spill && (rc = check_rows(h, contrib, &src))) return rc;
+  return run_step_bucketed(h, src, bucket_len, streams, ready, lr, t, global_sumsq_dev,
+                           use_spill);
+}
+
+int zero_shard_step_bucketed_q8(zs_handle *h, const int8_t *const *codes,
+                                const float *const *scales, int32_t block, int64_t bucket_len,
+                                int32_t streams, const void *const *ready, float lr, int64_t t,
+                                const double *global_sumsq_dev) {
+  Q8Rows src;
+  std::memset(&src, 0, sizeof src);
+  bool use_spill = false;
+  int rc = step_args_ok(h, lr, t, global_sumsq_dev, &use_spill);
+  if (rc) return rc;
+  if (quant_lanes(block) < 0) return ZS_EINVAL;
+  if ((rc = bucket_args_ok(h, bucket_len, streams))) return rc;
+  if (h->d.shard_len > 0 && !use_spill && (rc = check_q8(h, codes, scales, block, &src)))
+    return rc;
+  return run_step_bucketed(h, src, bucket_len, streams, ready, lr, t, global_sumsq_dev,
+                           use_spill);
 }
 
 int zero_shard_free(zs_handle *h) {

@@ -39,12 +39,6 @@ def _same(a: dict, b: dict) -> None:
         assert np.array_equal(x.view(np.uint8), y.view(np.uint8)), k
 
 
-def _bucket_rows(g: GpuShard, lo: int, hi: int):
-    """Bucket [lo, hi) of each contribution row (the views a caller's
-    per-bucket receive would fill)."""
-    return [g.rows_buf[k * g.stride + lo: k * g.stride + hi] for k in range(g.nd)]
-
-
 @pytest.mark.parametrize("name,n,bucket,streams,qb", [
     ("gpt2-small-flat", 300_001, 65_536, 2, 0),     # ragged last bucket
     ("gpt2-small-flat", 300_001, 512, 4, 256),      # many small buckets
@@ -208,3 +202,58 @@ def test_bucketed_empty_shard_and_errors():
     _same(before, g.host())
     g.free()
     assert Z.zero_shard_gnorm_bucketed(h, g.rows, 512, 2, None, g.sumsq) == Z.ZS_ESTATE
+
+
+@pytest.mark.parametrize("clip,bucket,streams", [
+    (0.0, 65_536, 2),
+    (0.0, 512 * 37, 3),
+    (0.05, 65_536, 2),
+    (0.05, 131_072, 4),
+])
+def test_bucketed_q8_equals_step_q8(clip, bucket, streams):
+    """int8 contributions (qgZ) bucket by bucket: bitwise equal to the
+    unbucketed _q8 step given the same S; S against the oracle's."""
+    import torch
+
+    w = dataclasses.replace(S.by_name("7.5B-nd64-zeropp"), n_d=16, max_norm=clip)
+    n, cb = 300_001, w.contrib_block
+    log(f"case bucketed q8 n={n} clip={clip} bucket={bucket} streams={streams}")
+    a, b = GpuShard(w, n=n), GpuShard(w, n=n)
+    a.init_state()
+    b.init_state()
+    for s in range(1, 4):
+        a.fill_grads(s)
+        b.fill_grads(s)
+        if clip > 0:
+            a.norm()
+            b.shard.gnorm_bucketed_q8(b.qrows, b.srows, cb, bucket, b.sumsq, streams=streams)
+            torch.cuda.synchronize()
+            codes, scales = S.host_contrib_q8(w, s, 0, n)
+            _, s_o = O.gbar_sumsq_q8(codes, scales, cb)
+            tol = P.sumsq_tolerance(n, s_o, buckets=-(-n // bucket))
+            assert abs(float(b.sumsq.item()) - s_o) <= tol
+            a.sumsq.copy_(b.sumsq)
+            a.update(s)
+            b.shard.step_bucketed_q8(None, None, cb, bucket, w.lr, w.t_of(s), b.sumsq,
+                                     streams=streams)
+        else:
+            a.step(s)
+            b.shard.step_bucketed_q8(b.qrows, b.srows, cb, bucket, w.lr, w.t_of(s),
+                                     streams=streams)
+    torch.cuda.synchronize()
+    _same(a.host(), b.host())
+    a.free()
+    b.free()
+
+
+def test_bucketed_q8_errors():
+    w = dataclasses.replace(S.by_name("7.5B-nd64-zeropp"), n_d=4)
+    g = GpuShard(w, n=4096)
+    h = g.shard.h
+    assert Z.zero_shard_step_bucketed_q8(h, g.qrows, g.srows, 100, 512, 2, None, 1e-3,
+                                         1) == Z.ZS_EINVAL
+    assert Z.zero_shard_step_bucketed_q8(h, g.qrows, g.srows, 256, 768, 2, None, 1e-3,
+                                         1) == Z.ZS_EINVAL
+    assert Z.zero_shard_gnorm_bucketed_q8(h, g.qrows, None, 256, 512, 2, None,
+                                          g.sumsq) == Z.ZS_EINVAL
+    g.free()
