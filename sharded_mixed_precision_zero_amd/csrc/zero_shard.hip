@@ -1247,14 +1247,6 @@ int run_step_bucketed(zs_handle *h, const Src &src, int64_t bucket_len, int32_t 
 
 extern "C" {
 
-int64_t zero_shard_len(int64_t phi, int32_t n_d, int32_t r) {
-  if (phi < 0 || n_d < 1 || r < 0 || r >= n_d) return -1;
-  const int64_t per = phi / n_d + (phi % n_d != 0);
-  const int64_t rest = phi - int64_t(r) * per;
-  if (rest <= 0) return 0;
-  return rest < per ? rest : per;
-}
-
 const char *zero_shard_strerror(int code) {
   switch (code) {
     case ZS_OK: return "ok";

@@ -1,5 +1,6 @@
-// zero_shard_host.cpp -- ZeRO-Offload host step (declared in
-// include/zero_shard.h: zero_shard_host_step).
+// zero_shard_host.cpp -- the library's host-only code (declared in
+// include/zero_shard.h): the ZeRO-Offload host step zero_shard_host_step,
+// and the partition geometry zero_shard_len.
 //
 // ZeRO-Offload keeps the optimizer states in host memory and runs the
 // update on the CPU ("ZeRO (딥 러닝)", follow-ups table "후속 기법":
@@ -134,6 +135,16 @@ bool have_avx512() {
 bool finite_pos(float x) { return std::isfinite(x) && x > 0.0f; }
 
 }  // namespace
+
+// Partition geometry (declared in include/zero_shard.h): ceil(phi / n_d)
+// elements per rank, the last partitions shorter or empty.
+extern "C" int64_t zero_shard_len(int64_t phi, int32_t n_d, int32_t r) {
+  if (phi < 0 || n_d < 1 || r < 0 || r >= n_d) return -1;
+  const int64_t per = phi / n_d + (phi % n_d != 0);
+  const int64_t rest = phi - int64_t(r) * per;
+  if (rest <= 0) return 0;
+  return rest < per ? rest : per;
+}
 
 extern "C" int zero_shard_host_step(const zs_desc *d, const float *gbar, float lr, int64_t t,
                                     double global_sumsq, int32_t threads) {
