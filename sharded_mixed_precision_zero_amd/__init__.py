@@ -132,6 +132,8 @@ def contrib_table(contrib) -> ctypes.Array | None:
     rows of a 2-D tensor (row k = rank k's contribution, codes or scales)."""
     if contrib is None:
         return None
+    if isinstance(contrib, ctypes.Array):  # already a table (kept by the caller)
+        return contrib
     if hasattr(contrib, "dim") and contrib.dim() == 2:
         rows = [contrib[k] for k in range(contrib.shape[0])]
     else:

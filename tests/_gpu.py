@@ -78,6 +78,11 @@ class GpuShard:
                                         dtype=torch.int16, device=DEV)
             self.rows = [self.rows_buf[k * self.stride: k * self.stride + n_]
                          for k in range(self.nd)]
+        # the host pointer tables the library takes, built once
+        if self.cb:
+            self.qtab, self.stab = Z.contrib_table(self.qrows), Z.contrib_table(self.srows)
+        else:
+            self.tab = Z.contrib_table(self.rows)
         if phi is None:
             phi, r = (w.phi, w.r) if n is None else (n_, 0)
         self.shard = Z.ZeroShard(
@@ -102,9 +107,9 @@ class GpuShard:
         """The clipped step's first sweep: this shard's sum of squares into
         self.sumsq (and the gradient spill when there is one)."""
         if self.cb:
-            self.shard.gnorm_q8(self.qrows, self.srows, self.cb, self.sumsq)
+            self.shard.gnorm_q8(self.qtab, self.stab, self.cb, self.sumsq)
         else:
-            self.shard.gnorm(self.rows, self.sumsq)
+            self.shard.gnorm(self.tab, self.sumsq)
 
     def update(self, s: int, lr: float | None = None) -> None:
         """The update of step s (1-based) on the resident contributions."""
@@ -112,10 +117,10 @@ class GpuShard:
         spill = self.clip and self.gbar_ws is not None
         ssq = self.sumsq if self.clip else None
         if self.cb:
-            self.shard.step_q8(None if spill else self.qrows, None if spill else self.srows,
+            self.shard.step_q8(None if spill else self.qtab, None if spill else self.stab,
                                self.cb, lr, self.w.t_of(s), ssq)
         else:
-            self.shard.step(None if spill else self.rows, lr, self.w.t_of(s), ssq)
+            self.shard.step(None if spill else self.tab, lr, self.w.t_of(s), ssq)
 
     def step(self, s: int, lr: float | None = None) -> None:
         """Step s (1-based): the norm sweep when clipping, then the update."""
