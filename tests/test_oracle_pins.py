@@ -371,6 +371,40 @@ def test_shard_concatenation_equals_unpartitioned():
     assert np.array_equal(np.concatenate([p[3].scales for p in parts]), whole[3].scales)
 
 
+def test_elastic_reslice_continues_bitwise():
+    """Re-sharding is a re-slice of the fp32 state (elementwise independence,
+    "ZeRO-1"): four shards stepped twice, concatenated, cut into two shards
+    and stepped twice more equal four shards stepped four times, when the
+    averaged gradient is the same (contributions in equal pairs: the mean
+    over [a, a, b, b] is exactly the mean over [a, b])."""
+    w = S.by_name("tiny-zero1")
+    phi = 100_003
+
+    def grads(s):
+        return [S.host_bf16(phi, w.seed, S.GRAD, s, k, 0, w.grad_sigma) for k in (0, 1)]
+
+    def run(state, nd, steps):
+        master, m, v = state
+        per = -(-phi // nd)
+        for s in steps:
+            a, b = grads(s)
+            src = [a, a, b, b] if nd == 4 else [a, b]
+            for r in range(nd):
+                lo, hi = r * per, min(phi, (r + 1) * per)
+                sl = slice(lo, hi)
+                mm, mo, va = master[sl].copy(), m[sl].copy(), v[sl].copy()
+                O.step([x[sl] for x in src], mm, mo, va,
+                       O.Hyper(lr=w.lr, weight_decay=0.1, t=s))
+                master[sl], m[sl], v[sl] = mm, mo, va
+        return master, m, v
+
+    ref = run(S.host_state(w, 0, phi), 4, range(1, 5))
+    mid = run(S.host_state(w, 0, phi), 4, range(1, 3))
+    got = run(mid, 2, range(3, 5))
+    for x, y in zip(ref, got):
+        assert np.array_equal(x.view(np.uint32), y.view(np.uint32))
+
+
 def test_step_thread_invariance():
     w = S.by_name("13B-nd16-clip-int8")
     n = (1 << 20) * 2 + 777
