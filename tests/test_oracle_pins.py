@@ -226,6 +226,56 @@ def test_adam_constant_gradient_closed_form():
         assert np.allclose(th, want, rtol=2e-6, atol=0), t
 
 
+def test_adam_warm_state_against_50_digit_evaluation():
+    """The general update (warm m and v, t > 1, decay, a clip coefficient)
+    evaluated in 50-digit decimal arithmetic from the same binary32 inputs
+    and binary32 hyper-parameters: the oracle's stored binary32 results are
+    the correctly rounded exact values to within one ulp (the binary64 path
+    rounds a few times before the final rounding), and almost always equal.
+    A dropped term, a wrong sign or a wrong bias-correction exponent moves
+    results by far more than an ulp."""
+    from decimal import Decimal, getcontext
+
+    getcontext().prec = 50
+    rng = np.random.default_rng(5)
+    n = 2000
+    theta = rng.normal(0, 0.02, n).astype(np.float32)
+    m = rng.normal(0, 1e-4, n).astype(np.float32)
+    v = np.abs(rng.normal(0, 1e-6, n)).astype(np.float32)
+    gbar = rng.normal(0, 1e-3, n).astype(np.float32)
+    gbar[:20] = 0.0
+    gbar[20:40] *= 1e-6  # |g| well below eps
+    coef, t = 0.37, 7
+    h = O.Hyper(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.1, t=t)
+    f = lambda x: Decimal(float(np.float32(x)))  # noqa: E731  the binary32 value, exactly
+    lr, b1, b2, eps, wd = f(h.lr), f(h.beta1), f(h.beta2), f(h.eps), f(h.weight_decay)
+    bc1, bc2 = 1 - b1 ** t, 1 - b2 ** t
+    c = Decimal(coef)
+    want = {"theta": [], "m": [], "v": []}
+    for i in range(n):
+        g = c * Decimal(float(gbar[i]))
+        m1 = b1 * Decimal(float(m[i])) + (1 - b1) * g
+        v1 = b2 * Decimal(float(v[i])) + (1 - b2) * g * g
+        th = Decimal(float(theta[i]))
+        t1 = th - lr * wd * th - lr * (m1 / bc1) / ((v1 / bc2).sqrt() + eps)
+        want["theta"].append(t1)
+        want["m"].append(m1)
+        want["v"].append(v1)
+    th_o, m_o, v_o = theta.copy(), m.copy(), v.copy()
+    O.adam(th_o, m_o, v_o, gbar, coef, h)
+    for name, got in (("theta", th_o), ("m", m_o), ("v", v_o)):
+        exact = want[name]
+        nearest = np.array([float(x) for x in exact], np.float64).astype(np.float32)
+        # np.float32(binary64) rounds twice; settle ties of the exact value
+        # directly: the distance in ulps of the oracle's result to the exact
+        ulp = np.spacing(np.abs(got)).astype(np.float64)
+        err = np.array([abs(Decimal(float(got[i])) - exact[i]) / Decimal(float(ulp[i]))
+                        if ulp[i] > 0 else Decimal(0) for i in range(n)], dtype=object)
+        assert all(e <= 1 for e in err), name
+        same = np.mean(got.view(np.uint32) == nearest.view(np.uint32))
+        assert same >= 0.99, (name, same)
+
+
 def test_adam_decoupled_weight_decay_alone():
     """g = 0 everywhere: m = v = 0, the Adam term is 0/(0+eps) = 0, and the
     decoupled decay gives theta_t = theta_0 (1 - lr wd)^t."""
