@@ -276,7 +276,7 @@ def main() -> int:
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one rank's shard step on one GPU; this build has no "
+        print("bench.py measures one rank's shard step on one GPU; there is no "
               "multi-GPU path (run with --gpus 1)", file=sys.stderr)
         return 2
 
