@@ -250,6 +250,119 @@ def bench_offload(w, args) -> int:
     return 0
 
 
+def bench_overlap(w, args) -> int:
+    """Buckets arriving over a link: bucket j's contributions arrive after
+    a wait of its bytes / --arrive-gbps on a separate stream (a stand-in for
+    the reduce-scatter's transfer; the wait moves no memory), and the
+    bucketed norm pass (with clipping; the whole fused step without) of
+    bucket j starts as soon as bucket j has arrived.  Against it: wait for
+    every bucket, then the unbucketed step.  Both are timed from the first
+    arrival's start to the end of the update."""
+    import torch
+
+    import seeded_inputs as S
+    from tests._gpu import GpuShard
+
+    n = w.shard_len
+    per = -(-int(args.bucket) // w.n_d)
+    bl = -(-per // 512) * 512
+    nb = -(-n // bl)
+    row = (1.0 + 4.0 / w.contrib_block) if w.contrib_block else 2.0
+    rate = args.arrive_gbps * 1e9
+    arrive_us = [min(bl, n - j * bl) * row * w.n_d / rate * 1e6 for j in range(nb)]
+    _eprint(f"[bench] overlap {w.name}: {nb} buckets of {bl}, arrival {sum(arrive_us) / 1e3:.2f} ms "
+            f"at {args.arrive_gbps} GB/s, {args.bucket_streams} worker streams")
+    g = GpuShard(w)
+    g.init_state()
+    g.fill_grads(1)
+    compute = torch.cuda.current_stream()
+    comm = torch.cuda.Stream()
+    use_spill = g.clip and g.gbar_ws is not None
+    ssq = g.sumsq if g.clip else None
+
+    def arrivals(record_each: bool):
+        comm.wait_stream(compute)  # the previous step is done with the rows
+        e0 = torch.cuda.Event(enable_timing=True)
+        e0.record(comm)
+        evs = []
+        for us in arrive_us:
+            S.dev_delay(us, comm)
+            if record_each:
+                e = torch.cuda.Event()
+                e.record(comm)
+                evs.append(e)
+        return e0, evs
+
+    def overlapped(s):
+        e0, evs = arrivals(True)
+        if g.cb:
+            if g.clip:
+                g.shard.gnorm_bucketed_q8(g.qtab, g.stab, g.cb, bl, g.sumsq,
+                                          streams=args.bucket_streams, ready=evs)
+            g.shard.step_bucketed_q8(None if use_spill else g.qtab, None if use_spill else g.stab,
+                                     g.cb, bl, w.lr, w.t_of(s), ssq, streams=args.bucket_streams,
+                                     ready=None if use_spill else evs)
+        else:
+            if g.clip:
+                g.shard.gnorm_bucketed(g.tab, bl, g.sumsq, streams=args.bucket_streams, ready=evs)
+            g.shard.step_bucketed(None if use_spill else g.tab, bl, w.lr, w.t_of(s), ssq,
+                                  streams=args.bucket_streams, ready=None if use_spill else evs)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e1.record(compute)
+        return e0, e1
+
+    def serial(s):
+        e0, _ = arrivals(False)
+        done = torch.cuda.Event()
+        done.record(comm)
+        compute.wait_event(done)
+        g.step(s)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e1.record(compute)
+        return e0, e1
+
+    def compute_only(s):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e0.record(compute)
+        g.step(s)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e1.record(compute)
+        return e0, e1
+
+    res = {}
+    for name, fn in (("compute_only", compute_only), ("serial", serial),
+                     ("overlapped", overlapped)):
+        for s in range(1, args.warmup + 1):
+            fn(s)
+        torch.cuda.synchronize()
+        evs = [fn(args.warmup + 1 + i) for i in range(args.steps)]
+        torch.cuda.synchronize()
+        res[name] = sum(a.elapsed_time(b) for a, b in evs) / len(evs)
+        _eprint(f"[bench] {name}: {res[name]:.3f} ms per step")
+    g.free()
+    arrival_ms = sum(arrive_us) / 1e3
+    hidden = (res["serial"] - res["overlapped"]) / min(arrival_ms, res["compute_only"])
+    line = {
+        "metric": "params updated/sec per ZeRO shard step with buckets arriving over a link "
+                  "(bucketed, overlapped)",
+        "value": n / (res["overlapped"] * 1e-3), "unit": "params/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": res["overlapped"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f64",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name} bucketed, arrival at {args.arrive_gbps} GB/s",
+                   "phi": w.phi, "n_d": w.n_d, "shard_len": n, "bucket_len": bl, "buckets": nb,
+                   "bucket_streams": args.bucket_streams, "arrive_gbps": args.arrive_gbps},
+        "overlap": {"arrival_ms": round(arrival_ms, 3),
+                    "compute_only_ms": round(res["compute_only"], 3),
+                    "serial_ms": round(res["serial"], 3),
+                    "overlapped_ms": round(res["overlapped"], 3),
+                    "hidden_frac": round(hidden, 3)},
+        "roofline": None, "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -271,6 +384,10 @@ def main() -> int:
                          "e.g. 5e8), i.e. ceil(ELEMS / n_d) shard elements per bucket rounded up "
                          "to 512, each on one of --bucket-streams worker streams")
     ap.add_argument("--bucket-streams", type=int, default=2)
+    ap.add_argument("--arrive-gbps", type=float, default=0.0, metavar="GBPS",
+                    help="with --bucket: buckets arrive over a link of GBPS GB/s (a timed wait "
+                         "per bucket on another stream), and the bucketed step overlaps the "
+                         "arrivals; compared with waiting for all buckets")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run torch copies of MIB MiB (for HBM counter scaling)")
     args = ap.parse_args()
@@ -305,6 +422,11 @@ def main() -> int:
         return bench_dequant(w, args)
     if args.offload:
         return bench_offload(w, args)
+    if args.arrive_gbps:
+        if not args.bucket:
+            _eprint("[bench] --arrive-gbps needs --bucket")
+            return 2
+        return bench_overlap(w, args)
     spill = not args.no_spill
     n = w.shard_len
     _eprint(f"[bench] workload {w.name}: shard {n} of phi {w.phi}, n_d {w.n_d}, "

@@ -58,6 +58,8 @@ def dev_lib() -> ctypes.CDLL:
         if not os.path.exists(DEV_LIB):
             raise RuntimeError(f"generator not built: {DEV_LIB} (run __graft_entry__.build())")
         L = ctypes.CDLL(DEV_LIB)
+        L.zsg_dev_delay.restype = ctypes.c_int
+        L.zsg_dev_delay.argtypes = [ctypes.c_double, ctypes.c_void_p]
         L.zsg_dev_fill_f32.restype = ctypes.c_int
         L.zsg_dev_fill_f32.argtypes = [_vp, _i64, _u64, _u32, _u32, _u32, _i64, _f32,
                                        ctypes.c_int, ctypes.c_int, _vp]
@@ -173,6 +175,12 @@ def dev_bf16(t, seed: int, tid: int, step: int, rank: int, i0: int, sigma: float
     _check(dev_lib().zsg_dev_fill_bf16(t.data_ptr(), t.numel(), seed, tid, step, rank, int(i0),
                                        float(sigma), int(outliers), _stream(stream)),
            "zsg_dev_fill_bf16")
+
+
+def dev_delay(usec: float, stream=None) -> None:
+    """Queue a wait of usec microseconds on `stream` (the arrival time of a
+    bucket of inputs whose transfer is not modelled as memory traffic)."""
+    _check(dev_lib().zsg_dev_delay(float(usec), _stream(stream)), "zsg_dev_delay")
 
 
 def dev_contrib(w: Workload, step: int, buf, n: int, row_stride: int, i0: int = 0,

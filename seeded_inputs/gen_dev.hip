@@ -32,6 +32,18 @@ fill_code(int8_t *out, int64_t n, uint64_t h, int64_t i0) {
     out[j] = zsg_code(h, uint64_t(i0 + j));
 }
 
+// Stands for the time a bucket of inputs takes to arrive over a link whose
+// traffic does not touch this GPU's memory: one wave waits on the
+// constant-rate wall clock for `ticks`, sleeping between reads.  The loop
+// is bounded (at most 2^28 sleeps of 8 x 64 cycles).
+__global__ void __launch_bounds__(64) delay_kernel(uint64_t ticks) {
+  const uint64_t t0 = wall_clock64();
+  for (uint32_t it = 0; it < (1u << 28); ++it) {
+    if (wall_clock64() - t0 >= ticks) break;
+    __builtin_amdgcn_s_sleep(8);
+  }
+}
+
 unsigned grid_for(int64_t n) {
   int64_t b = (n + kThreads - 1) / kThreads;
   if (b > 65536) b = 65536;
@@ -97,6 +109,18 @@ int zsg_dev_fill_contrib_q8(void *codes, void *scales, int32_t n_d, int64_t code
     if (hipGetLastError() != hipSuccess) return -4;
   }
   return 0;
+}
+
+/* Queue a wait of `usec` microseconds (0 < usec <= 1e6) on `stream`. */
+int zsg_dev_delay(double usec, void *stream) {
+  if (!(usec > 0.0) || usec > 1e6) return -1;
+  int dev = -1, khz = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return -4;
+  if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess || khz <= 0)
+    return -4;
+  const uint64_t ticks = uint64_t(usec * double(khz) / 1000.0);
+  hipLaunchKernelGGL(delay_kernel, dim3(1), dim3(64), 0, hipStream_t(stream), ticks);
+  return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 
 }  // extern "C"

@@ -257,3 +257,44 @@ def test_bucketed_q8_errors():
     assert Z.zero_shard_gnorm_bucketed_q8(h, g.qrows, None, 256, 512, 2, None,
                                           g.sumsq) == Z.ZS_EINVAL
     g.free()
+
+
+def test_arrival_delay_waits_and_bucketed_step_waits_for_it():
+    """The arrival stand-in (a bounded wait on the wall clock) takes about
+    the time asked for, and a bucketed step that waits on events recorded
+    after such waits gives the unbucketed step's bits."""
+    import torch
+
+    comm = torch.cuda.Stream()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(comm)
+    S.dev_delay(2000.0, comm)
+    b.record(comm)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b)
+    assert 1.9 <= ms <= 4.0, ms
+
+    w = dataclasses.replace(S.by_name("13B-nd16-clip-int8"), max_norm=0.05)
+    n, bucket = 300_001, 65_536
+    g1, g2 = GpuShard(w, n=n), GpuShard(w, n=n)
+    g1.init_state()
+    g2.init_state()
+    for s in (1, 2):
+        g1.fill_grads(s)
+        g2.fill_grads(s)
+        g1.norm()
+        comm.wait_stream(torch.cuda.current_stream())
+        evs = []
+        for _ in range(-(-n // bucket)):
+            S.dev_delay(300.0, comm)
+            e = torch.cuda.Event()
+            e.record(comm)
+            evs.append(e)
+        g2.shard.gnorm_bucketed(g2.rows, bucket, g2.sumsq, streams=2, ready=evs)
+        g1.sumsq.copy_(g2.sumsq)
+        g1.update(s)
+        g2.shard.step_bucketed(None, bucket, w.lr, w.t_of(s), g2.sumsq, streams=2)
+    torch.cuda.synchronize()
+    _same(g1.host(), g2.host())
+    g1.free()
+    g2.free()
