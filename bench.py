@@ -181,58 +181,93 @@ def bench_dequant(w, args) -> int:
 
 
 def bench_offload(w, args) -> int:
-    """ZeRO-Offload step: the norm pass on the GPU leaves the averaged
-    gradient in HBM, it is downloaded to pinned host memory, the update runs
-    on host threads over host-resident fp32 state (zero_shard_host_step) and
-    the bf16 copy is uploaded; with the one-step delayed update the host
-    update of step s overlaps the GPU work of step s+1."""
+    """ZeRO-Offload step through the library's pipeline (zero_shard_offload_*):
+    the norm pass on the GPU leaves the averaged gradient in HBM, it is
+    downloaded to pinned host memory, the update runs on host threads over
+    host-resident state and the bf16 parameters are uploaded; the host
+    update of step s overlaps the caller's next step (one-step delayed
+    update).  Also times each stage alone on the same data."""
+    import statistics
+
     import torch
 
+    import sharded_mixed_precision_zero_amd as Z
     from tests._gpu import OffloadShard
 
     if w.contrib_block:
         _eprint("[bench] --offload takes bf16 contributions; this workload's are int8")
         return 2
     threads = min(16, len(os.sched_getaffinity(0)))
-    _eprint(f"[bench] offload {w.name}: shard {w.shard_len}, host threads {threads}")
+    n = w.shard_len
+    _eprint(f"[bench] offload {w.name}: shard {n}, host threads {threads}")
     off = OffloadShard(w, threads=threads)
     off.fill_grads(1)
     torch.cuda.synchronize()
-    _eprint("[bench] offload inputs resident; warmup")
     for s in range(1, args.warmup + 1):
-        off.step(s, delayed=True)
+        off.step(s)
     off.finish()
     torch.cuda.synchronize()
-    off.timed = True
     t0 = time.perf_counter()
     for i in range(args.steps):
-        off.step(args.warmup + 1 + i, delayed=True)
+        off.step(args.warmup + 1 + i)
     off.finish()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    n = w.shard_len
+    ms_step = elapsed * 1e3 / args.steps
 
-    def mean_ms(pairs):
-        return sum(a.elapsed_time(b) for a, b in pairs) / len(pairs)
+    # each stage alone, on the same buffers
+    stream = torch.cuda.current_stream()
+    spill = torch.empty(n, dtype=torch.float32, device="cuda")
+    ssq = torch.zeros(1, dtype=torch.float64, device="cuda")
+    norm_only = Z.ZeroShard(phi=w.phi, n_d=w.n_d, r=w.r, shard_len=n, master=None, m=None,
+                            v=None, param_out=None, beta1=w.beta1, beta2=w.beta2, eps=w.eps,
+                            weight_decay=w.weight_decay, max_norm=w.max_norm, gbar_ws=spill)
+    g_host = torch.empty(n, dtype=torch.float32, pin_memory=True)
+    p_host = torch.empty(n, dtype=torch.int16, pin_memory=True)
+    p_dev = torch.empty(n, dtype=torch.int16, device="cuda")
 
-    norm_ms, d2h_ms, h2d_ms = mean_ms(off.ev_norm), mean_ms(off.ev_d2h), mean_ms(off.ev_h2d)
-    host_ms = 1e3 * sum(off.host_s) / len(off.host_s)
+    def timed(fn, reps=5):
+        out = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+            out.append(a.elapsed_time(b))
+        return statistics.median(out)
+
+    norm_ms = timed(lambda: norm_only.gnorm(off.tab, ssq))
+    d2h_ms = timed(lambda: g_host.copy_(spill, non_blocking=True))
+    h2d_ms = timed(lambda: p_dev.copy_(p_host, non_blocking=True))
+    desc = Z.host_desc(phi=w.phi, n_d=w.n_d, r=w.r, shard_len=n, master=off.master, m=off.m,
+                       v=off.v, param_out=p_host, beta1=w.beta1, beta2=w.beta2, eps=w.eps,
+                       weight_decay=w.weight_decay, max_norm=w.max_norm,
+                       quant_block=w.quant_block, q_codes=off.codes, q_scales=off.scales)
+    host = []
+    for i in range(3):
+        t1 = time.perf_counter()
+        rc = Z.zero_shard_host_step(desc, g_host.data_ptr(), w.lr, 10_000 + i,
+                                    float(ssq.item()), threads)
+        host.append((time.perf_counter() - t1) * 1e3)
+        assert rc == 0
+    host_ms = statistics.median(host)
+    norm_only.free()
+    off.free()
     q = (1.0 + 4.0 / w.quant_block) if w.quant_block else 0.0
     host_bpp = 4.0 + 24.0 + 2.0 + q
-    norm_bpp = 2.0 * w.n_d + 4.0
-    norm_gbs = norm_bpp * n / (norm_ms * 1e-3) / 1e9
+    norm_gbs = (2.0 * w.n_d + 4.0) * n / (norm_ms * 1e-3) / 1e9
     d2h_gbs = 4.0 * n / (d2h_ms * 1e-3) / 1e9
     h2d_gbs = 2.0 * n / (h2d_ms * 1e-3) / 1e9
     host_gbs = host_bpp * n / (host_ms * 1e-3) / 1e9
-    _eprint(f"[bench] offload step {elapsed * 1e3 / args.steps:.2f} ms: GPU norm {norm_ms:.3f} ms "
+    _eprint(f"[bench] offload step {ms_step:.2f} ms; alone: GPU norm {norm_ms:.3f} ms "
             f"({norm_gbs:.0f} GB/s), spill download {d2h_ms:.2f} ms ({d2h_gbs:.1f} GB/s), "
             f"host update {host_ms:.2f} ms ({host_gbs:.1f} GB/s of host memory), "
             f"bf16 upload {h2d_ms:.2f} ms ({h2d_gbs:.1f} GB/s)")
-    off.free()
     line = {
         "metric": "params updated/sec per ZeRO-Offload shard step (host Adam, one-step delay)",
-        "value": n / (elapsed / args.steps), "unit": "params/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": elapsed * 1e3 / args.steps,
+        "value": n / (ms_step * 1e-3), "unit": "params/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f64",
         "data": "synthetic",
         "config": {"workload": f"{w.name} offload", "phi": w.phi, "n_d": w.n_d,

@@ -241,6 +241,45 @@ int zero_shard_dequant(const int8_t *const *codes, const float *const *scales, i
 int zero_shard_host_step(const zs_desc *d, const float *gbar, float lr, int64_t t,
                          double global_sumsq, int32_t threads);
 
+/* ZeRO-Offload pipeline for one rank's shard ("ZeRO (딥 러닝)", follow-ups
+ * table "후속 기법": optimizer states and their update on the CPU, the
+ * update hidden behind the GPU's next step by a one-step delayed update).
+ *
+ * zero_shard_offload_init: `host` describes the shard with HOST pointers
+ * for master/m/v (and q_codes/q_scales when quant_block > 0), as for
+ * zero_shard_host_step; its param_out, gbar_ws and stream are ignored.
+ * param_dev0/param_dev1 are two device bf16[shard_len] buffers (16-byte
+ * aligned) that the updated parameters are uploaded into, alternately;
+ * `stream` is the caller's compute stream; `threads` (>= 1) host threads
+ * run the update.  The library allocates a device spill and S scalar, two
+ * pinned gradient slots and two pinned bf16 slots, and a download and an
+ * upload stream.
+ *
+ * zero_shard_offload_step: step t.  Queues on `stream` the norm pass over
+ * contrib (a HOST array of n_d device pointers, as for zero_shard_gnorm),
+ * then copies the averaged gradient and S_local to pinned memory, waits
+ * for the host update of the previous step to finish, orders `stream`
+ * after that step's upload, starts this step's host update (a3-a5 with
+ * S = S_local + s_other, s_other >= 0 being the other shards' sum) on a
+ * host thread, and returns.  The host update uploads its bf16 parameters
+ * into buffer (call index mod 2).  Work queued on `stream` after the call
+ * sees the parameters of the previous step: zero_shard_offload_params
+ * names that buffer (NULL before any update has been uploaded).
+ * zero_shard_offload_wait: finish the running host update and order
+ * `stream` after its upload; zero_shard_offload_params then names the
+ * newest parameters.  Errors of a host update are returned by the next
+ * step or wait call.  zero_shard_offload_free waits and releases.
+ * The results are those of zero_shard_step on the same inputs, bit for bit.
+ * Errors: ZS_EINVAL, ZS_EALIGN, ZS_ENOMEM, ZS_EHIP, ZS_ESTATE. */
+typedef struct zs_offload zs_offload;
+int zero_shard_offload_init(const zs_desc *host, zs_bf16 *param_dev0, zs_bf16 *param_dev1,
+                            void *stream, int32_t threads, zs_offload **out);
+int zero_shard_offload_step(zs_offload *o, const zs_bf16 *const *contrib, float lr, int64_t t,
+                            double s_other);
+zs_bf16 *zero_shard_offload_params(zs_offload *o);
+int zero_shard_offload_wait(zs_offload *o);
+int zero_shard_offload_free(zs_offload *o);
+
 /* Wait for the handle's stream, release its scratch and the handle.
  * Passing NULL is a no-op returning ZS_OK. */
 int zero_shard_free(zs_handle *h);

@@ -94,6 +94,19 @@ _lib.zero_shard_dequant.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_i
 _lib.zero_shard_host_step.restype = ctypes.c_int
 _lib.zero_shard_host_step.argtypes = [ctypes.POINTER(zs_desc), ctypes.c_void_p, ctypes.c_float,
                                       ctypes.c_int64, ctypes.c_double, ctypes.c_int32]
+_lib.zero_shard_offload_init.restype = ctypes.c_int
+_lib.zero_shard_offload_init.argtypes = [ctypes.POINTER(zs_desc), ctypes.c_void_p,
+                                         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
+                                         ctypes.POINTER(_handle_p)]
+_lib.zero_shard_offload_step.restype = ctypes.c_int
+_lib.zero_shard_offload_step.argtypes = [_handle_p, ctypes.c_void_p, ctypes.c_float,
+                                         ctypes.c_int64, ctypes.c_double]
+_lib.zero_shard_offload_params.restype = ctypes.c_void_p
+_lib.zero_shard_offload_params.argtypes = [_handle_p]
+_lib.zero_shard_offload_wait.restype = ctypes.c_int
+_lib.zero_shard_offload_wait.argtypes = [_handle_p]
+_lib.zero_shard_offload_free.restype = ctypes.c_int
+_lib.zero_shard_offload_free.argtypes = [_handle_p]
 _lib.zero_shard_quant.restype = ctypes.c_int
 _lib.zero_shard_quant.argtypes = [_handle_p, ctypes.c_int32]
 _lib.zero_shard_free.restype = ctypes.c_int
@@ -107,7 +120,9 @@ EXPORTS = ("zero_shard_init", "zero_shard_gnorm", "zero_shard_step", "zero_shard
            "zero_shard_step_q8", "zero_shard_gnorm_bucketed", "zero_shard_step_bucketed",
            "zero_shard_gnorm_bucketed_q8", "zero_shard_step_bucketed_q8",
            "zero_shard_quant", "zero_shard_dequant",
-           "zero_shard_host_step", "zero_shard_free", "zero_shard_strerror", "zero_shard_len")
+           "zero_shard_host_step", "zero_shard_offload_init", "zero_shard_offload_step",
+           "zero_shard_offload_params", "zero_shard_offload_wait", "zero_shard_offload_free",
+           "zero_shard_free", "zero_shard_strerror", "zero_shard_len")
 
 
 class ZeroShardError(RuntimeError):
@@ -259,6 +274,38 @@ def host_desc(*, phi: int, n_d: int, r: int, shard_len: int, master, m, v, param
                    quant_block=int(quant_block), master=addr(master), m=addr(m), v=addr(v),
                    param_out=addr(param_out), q_codes=addr(q_codes), q_scales=addr(q_scales),
                    gbar_ws=None, stream=None)
+
+
+def zero_shard_offload_init(host: zs_desc, param_dev0, param_dev1, stream=None,
+                            threads: int = 16):
+    """-> (status, handle).  host: a host_desc(...); param_dev0/1: 16-bit
+    device tensors of shard_len elements; stream: a torch stream (default:
+    the current one)."""
+    if stream is None:
+        import torch
+
+        stream = torch.cuda.current_stream()
+    o = _handle_p()
+    rc = _lib.zero_shard_offload_init(ctypes.byref(host), _ptr(param_dev0), _ptr(param_dev1),
+                                      int(stream.cuda_stream), int(threads), ctypes.byref(o))
+    return rc, o
+
+
+def zero_shard_offload_step(o, contrib, lr: float, t: int, s_other: float = 0.0) -> int:
+    return _lib.zero_shard_offload_step(o, contrib_table(contrib), float(lr), int(t),
+                                        float(s_other))
+
+
+def zero_shard_offload_params(o) -> int | None:
+    return _lib.zero_shard_offload_params(o)
+
+
+def zero_shard_offload_wait(o) -> int:
+    return _lib.zero_shard_offload_wait(o)
+
+
+def zero_shard_offload_free(o) -> int:
+    return _lib.zero_shard_offload_free(o)
 
 
 def zero_shard_free(h) -> int:

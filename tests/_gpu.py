@@ -14,7 +14,6 @@ from the seeded generator (device and host builds of one definition).
 from __future__ import annotations
 
 import sys
-import time
 
 import numpy as np
 
@@ -233,137 +232,67 @@ def windows(n: int, count: int, size: int, seed: int, extra: tuple = ()) -> list
 
 
 class OffloadShard:
-    """ZeRO-Offload for one rank's shard: the contributions and the norm
-    pass on the GPU (the averaged gradient lands in the device spill), the
-    fp32 optimizer state in host memory and the update on host threads
-    (zero_shard_host_step), the bf16 copy uploaded back for the next
-    forward pass.  With `delayed`, the host update of step s overlaps the
-    GPU's work for step s+1 (the one-step delayed update): two pinned
-    gradient slots and two pinned bf16 slots, a copy stream, events between
-    them."""
+    """ZeRO-Offload for one rank's shard through the library's native
+    pipeline (zero_shard_offload_*): the contributions and the norm pass on
+    the GPU, the fp32 optimizer state in host memory and its update on host
+    threads, the bf16 parameters uploaded into two alternating device
+    buffers, the host update of step s overlapping the caller's work after
+    the call (the one-step delayed update)."""
 
     def __init__(self, w: S.Workload, n: int | None = None, threads: int = 16):
-        import threading  # noqa: F401
-
         import torch
 
         self.torch, self.w = torch, w
         self.n = w.shard_len if n is None else int(n)
-        self.threads = threads
         n_ = self.n
         self.nd = w.n_d
         self.stride = row_stride(n_)
         self.rows_buf = torch.empty(max(1, (self.nd - 1) * self.stride + n_), dtype=torch.int16,
                                     device=DEV)
         self.rows = [self.rows_buf[k * self.stride: k * self.stride + n_] for k in range(self.nd)]
-        self.gbar_dev = torch.empty(n_, dtype=torch.float32, device=DEV)
-        self.sumsq_dev = torch.zeros(1, dtype=torch.float64, device=DEV)
-        self.p_dev = torch.empty(n_, dtype=torch.int16, device=DEV)
+        self.tab = Z.contrib_table(self.rows)
         phi, r = (w.phi, w.r) if n is None else (n_, 0)
-        # a norm-only device handle: the state is not on the GPU
-        self.shard = Z.ZeroShard(phi=phi, n_d=self.nd, r=r, shard_len=n_, master=None, m=None,
-                                 v=None, param_out=None, beta1=w.beta1, beta2=w.beta2, eps=w.eps,
-                                 weight_decay=w.weight_decay, max_norm=w.max_norm,
-                                 gbar_ws=self.gbar_dev)
         self.master, self.m, self.v = S.host_state(w, 0, n_)
-        # two pinned bf16 slots: the upload of step s-1 overlaps the host
-        # update of step s
-        self.p_host = [torch.empty(n_, dtype=torch.int16, pin_memory=True) for _ in range(2)]
         self.codes = np.empty(n_, np.int8) if w.quant_block else None
         self.scales = np.empty(-(-n_ // w.quant_block), np.float32) if w.quant_block else None
-        self.desc = [Z.host_desc(phi=phi, n_d=self.nd, r=r, shard_len=n_, master=self.master,
-                                 m=self.m, v=self.v, param_out=self.p_host[k], beta1=w.beta1,
-                                 beta2=w.beta2, eps=w.eps, weight_decay=w.weight_decay,
-                                 max_norm=w.max_norm, quant_block=w.quant_block,
-                                 q_codes=self.codes, q_scales=self.scales) for k in range(2)]
-        self.gbar_host = [torch.empty(n_, dtype=torch.float32, pin_memory=True) for _ in range(2)]
-        self.sumsq_host = [torch.zeros(1, dtype=torch.float64, pin_memory=True) for _ in range(2)]
-        self.compute = torch.cuda.current_stream()
-        self.copy = torch.cuda.Stream()
-        self.copied = [torch.cuda.Event() for _ in range(2)]
-        self.uploaded = [torch.cuda.Event() for _ in range(2)]
-        for e in self.uploaded:
-            e.record(self.copy)
-        self._worker = None
-        # per-step timings: host update seconds, and (start, end) timing
-        # events of the norm pass, the spill download and the bf16 upload
-        self.timed = False
-        self.host_s: list[float] = []
-        self.ev_norm: list = []
-        self.ev_d2h: list = []
-        self.ev_h2d: list = []
-
-    def _ev(self, log_, stream, first: bool) -> None:
-        if not self.timed:
-            return
-        e = self.torch.cuda.Event(enable_timing=True)
-        e.record(stream)
-        if first:
-            log_.append([e])
-        else:
-            log_[-1].append(e)
+        self.desc = Z.host_desc(phi=phi, n_d=self.nd, r=r, shard_len=n_, master=self.master,
+                                m=self.m, v=self.v, param_out=None, beta1=w.beta1,
+                                beta2=w.beta2, eps=w.eps, weight_decay=w.weight_decay,
+                                max_norm=w.max_norm, quant_block=w.quant_block,
+                                q_codes=self.codes, q_scales=self.scales)
+        self.p_dev = [torch.empty(max(1, n_), dtype=torch.int16, device=DEV) for _ in range(2)]
+        rc, self.o = Z.zero_shard_offload_init(self.desc, self.p_dev[0], self.p_dev[1],
+                                               threads=threads)
+        if rc:
+            raise Z.ZeroShardError(rc, "zero_shard_offload_init")
 
     def fill_grads(self, s: int) -> None:
         S.dev_contrib(self.w, s, self.rows_buf, self.n, self.stride)
 
-    def gpu_part(self, s: int) -> None:
-        """Norm pass of step s on the GPU, then its spill and S to host slot
-        s % 2 on the copy stream."""
-        torch, slot = self.torch, s % 2
-        # the spill of step s-1 must have left the device before it is reused
-        self.compute.wait_event(self.copied[1 - slot])
-        self._ev(self.ev_norm, self.compute, True)
-        self.shard.gnorm(self.rows, self.sumsq_dev)
-        self._ev(self.ev_norm, self.compute, False)
-        self.copy.wait_stream(self.compute)
-        self._ev(self.ev_d2h, self.copy, True)
-        with torch.cuda.stream(self.copy):
-            self.gbar_host[slot].copy_(self.gbar_dev, non_blocking=True)
-            self.sumsq_host[slot].copy_(self.sumsq_dev, non_blocking=True)
-        self._ev(self.ev_d2h, self.copy, False)
-        self.copied[slot].record(self.copy)
-
-    def cpu_part(self, s: int) -> None:
-        """Host update of step s from slot s % 2, then the bf16 upload."""
-        slot = s % 2
-        self.copied[slot].synchronize()
-        self.uploaded[slot].synchronize()  # the upload of step s-2 has read p_host[slot]
-        t0 = time.perf_counter()
-        rc = Z.zero_shard_host_step(self.desc[slot], self.gbar_host[slot].data_ptr(), self.w.lr,
-                                    self.w.t_of(s), float(self.sumsq_host[slot].item()),
-                                    self.threads)
+    def step(self, s: int, delayed: bool = True) -> None:
+        """Step s; without `delayed`, also wait for its host update."""
+        rc = Z.zero_shard_offload_step(self.o, self.tab, self.w.lr, self.w.t_of(s))
         if rc:
-            raise Z.ZeroShardError(rc, "zero_shard_host_step")
-        if self.timed:
-            self.host_s.append(time.perf_counter() - t0)
-        self._ev(self.ev_h2d, self.copy, True)
-        with self.torch.cuda.stream(self.copy):
-            self.p_dev.copy_(self.p_host[slot], non_blocking=True)
-        self._ev(self.ev_h2d, self.copy, False)
-        self.uploaded[slot].record(self.copy)
-
-    def step(self, s: int, delayed: bool = False) -> None:
-        """Step s.  delayed: return once the GPU part is queued and the host
-        update of step s-1 has finished; the host update of step s runs on a
-        worker thread, overlapping the next step's GPU work."""
-        import threading
-
-        self.gpu_part(s)
+            raise Z.ZeroShardError(rc, "zero_shard_offload_step")
         if not delayed:
-            self.cpu_part(s)
-            return
-        if self._worker is not None:
-            self._worker.join()
-        self._worker = threading.Thread(target=self.cpu_part, args=(s,))
-        self._worker.start()
+            self.finish()
 
     def finish(self) -> None:
-        if self._worker is not None:
-            self._worker.join()
-            self._worker = None
-        for e in self.uploaded:
-            e.synchronize()
+        rc = Z.zero_shard_offload_wait(self.o)
+        if rc:
+            raise Z.ZeroShardError(rc, "zero_shard_offload_wait")
+
+    def params(self):
+        """The device buffer holding the newest uploaded parameters."""
+        ptr = Z.zero_shard_offload_params(self.o)
+        for t in self.p_dev:
+            if t.data_ptr() == ptr:
+                return t
+        return None
 
     def free(self) -> None:
-        self.finish()
-        self.shard.free()
+        if self.o is not None and self.o.value:
+            rc = Z.zero_shard_offload_free(self.o)
+            if rc:
+                raise Z.ZeroShardError(rc, "zero_shard_offload_free")
+        self.o = None

@@ -437,8 +437,60 @@ def test_offload_equals_on_device_step(delayed):
     assert np.array_equal(got["master"].view(np.uint32), off.master.view(np.uint32))
     assert np.array_equal(got["m"].view(np.uint32), off.m.view(np.uint32))
     assert np.array_equal(got["v"].view(np.uint32), off.v.view(np.uint32))
-    assert np.array_equal(got["p"], off.p_dev.cpu().numpy().view(np.uint16))
+    assert np.array_equal(got["p"], off.params().cpu().numpy().view(np.uint16))
     assert np.array_equal(got["codes"], off.codes)
     assert np.array_equal(got["scales"].view(np.uint32), off.scales.view(np.uint32))
     off.free()
+    g.free()
+
+
+def test_offload_delayed_parameters_and_errors():
+    """After the call for step s, work on the caller's stream sees the
+    parameters of step s-1 (the one-step delayed update); after a wait, those
+    of step s.  Invalid calls return errors and change nothing."""
+    import torch
+
+    from tests._gpu import OffloadShard
+
+    w = _variant("gpt2-small-flat", quant_block=0)
+    n = 50_000 + 3
+    g = GpuShard(w, n=n)
+    g.init_state()
+    seen = {}
+    for s in range(1, 4):
+        g.fill_grads(s)
+        g.step(s)
+        seen[s] = g.host()["p"].copy()
+    off = OffloadShard(w, n=n, threads=4)
+    assert off.params() is None
+    for s in range(1, 4):
+        off.fill_grads(s)
+        off.step(s)
+        if s == 1:
+            assert off.params() is None
+        else:
+            got = off.params().cpu().numpy().view(np.uint16)  # ordered on the stream
+            assert np.array_equal(got, seen[s - 1]), s
+    off.finish()
+    assert np.array_equal(off.params().cpu().numpy().view(np.uint16), seen[3])
+    o = off.o
+    assert Z.zero_shard_offload_step(o, off.tab, -1.0, 4) == Z.ZS_EINVAL
+    assert Z.zero_shard_offload_step(o, off.tab, 1e-3, 0) == Z.ZS_EINVAL
+    assert Z.zero_shard_offload_step(o, off.tab, 1e-3, 4, float("nan")) == Z.ZS_EINVAL
+    assert Z.zero_shard_offload_step(o, None, 1e-3, 4) == Z.ZS_EINVAL
+    off.free()
+    assert Z.zero_shard_offload_step(o, off.tab, 1e-3, 4) == Z.ZS_ESTATE
+    assert Z.zero_shard_offload_wait(o) == Z.ZS_ESTATE
+    assert Z.zero_shard_offload_free(o) == Z.ZS_ESTATE
+    bad = torch.empty(n + 8, dtype=torch.int16, device="cuda")
+    desc = Z.host_desc(phi=n, n_d=w.n_d, r=0, shard_len=n, master=off.master, m=off.m,
+                       v=off.v, param_out=None)
+    rc, _ = Z.zero_shard_offload_init(desc, bad[1:], bad, threads=2)
+    assert rc == Z.ZS_EALIGN
+    rc, _ = Z.zero_shard_offload_init(desc, bad, bad, threads=0)
+    assert rc == Z.ZS_EINVAL
+    nod = Z.host_desc(phi=n, n_d=w.n_d, r=0, shard_len=n, master=None, m=off.m, v=off.v,
+                      param_out=None)
+    rc, _ = Z.zero_shard_offload_init(nod, bad, bad, threads=2)
+    assert rc == Z.ZS_EINVAL
     g.free()

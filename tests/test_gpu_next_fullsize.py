@@ -97,7 +97,7 @@ def test_offload_full_size():
     for name, dev, host in (("master", g.master, off.master), ("m", g.m, off.m),
                             ("v", g.v, off.v)):
         assert np.array_equal(dev.cpu().numpy().view(np.uint32), host.view(np.uint32)), name
-    assert torch.equal(g.p, off.p_dev)
+    assert torch.equal(g.p, off.params())
     assert np.array_equal(g.codes.cpu().numpy(), off.codes)
     assert np.array_equal(g.scales.cpu().numpy().view(np.uint32), off.scales.view(np.uint32))
     off.free()
