@@ -123,9 +123,9 @@ int zero_shard_init(const zs_desc *d, zs_handle **out);
 
 /* a2, first sweep: this shard's sum of squares of the averaged gradient,
  * S_local = sum_i gbar_i^2 (binary64), reduced over a grid fixed by the
- * shard length, in a fixed order, with no atomics (same inputs => same bits).  contrib is a HOST
- * array of n_d device pointers, contrib[k] = rank k's bf16 gradient for
- * this shard (shard-local index).  Writes S_local to *sumsq_dev (device,
+ * shard length, in a fixed order, with no atomics (same inputs => same
+ * bits).  contrib is a HOST array of n_d device pointers, contrib[k] =
+ * rank k's bf16 gradient for this shard (shard-local index).  Writes S_local to *sumsq_dev (device,
  * one double).  With gbar_ws set, also stores gbar there for the next step.
  * Summing S_local over the shards (one scalar all-reduce across ranks) gives
  * the S that zero_shard_step takes.  Errors: ZS_EINVAL, ZS_EALIGN, ZS_EHIP,
@@ -137,7 +137,10 @@ int zero_shard_gnorm(zs_handle *h, const zs_bf16 *const *contrib, double *sumsq_
  * be NULL when clipping with gbar_ws (the spill written by the preceding
  * zero_shard_gnorm is read instead).  global_sumsq_dev (device, one double)
  * is S and is required iff max_norm > 0; it is read on the device, so no
- * host synchronisation is needed between gnorm and step.
+ * host synchronisation is needed between gnorm and step.  gnorm and step
+ * queue kernel launches only (no allocation, no memset), so they can be
+ * captured in a HIP graph on the handle's stream; t and lr are then fixed
+ * in the captured launches.
  * Errors: ZS_EINVAL, ZS_EALIGN, ZS_ESTATE, ZS_EHIP. */
 int zero_shard_step(zs_handle *h, const zs_bf16 *const *contrib, float lr, int64_t t,
                     const double *global_sumsq_dev);
