@@ -2,13 +2,15 @@
 the smoke check and the benchmark's CPU baseline.
 
 ``GpuShard`` owns the device tensors of one shard (state, outputs, the
-N_d contribution rows) and calls the library through its C ABI.
-The oracle is imported only by the oracle-side helpers, so the benchmark
-can drive ``GpuShard`` without loading it.  ``OracleWindow`` evolves any window [i0, i0+n) of the same shard on the CPU
-with the oracle; unclipped steps are elementwise, so a window needs only
-its own inputs, and with clipping the caller supplies the global sum of
-squares computed by ``oracle_global_sumsq``.  Inputs on both sides come
-from the seeded generator (device and host builds of one definition).
+N_d contribution rows) and calls the library through its C ABI;
+``OffloadShard`` drives the library's ZeRO-Offload pipeline.  The oracle
+is imported only by the oracle-side helpers, so the benchmark can drive
+``GpuShard`` without loading it.  ``OracleWindow`` evolves any window
+[i0, i0+n) of the same shard on the CPU with the oracle; unclipped steps
+are elementwise, so a window needs only its own inputs, and with clipping
+the caller supplies the global sum of squares computed by
+``oracle_global_sumsq``.  Inputs on both sides come from the seeded
+generator (device and host builds of one definition).
 """
 
 from __future__ import annotations
