@@ -76,12 +76,15 @@ def dev_lib() -> ctypes.CDLL:
     return _dev
 
 
-def _threads() -> int:
+def _threads(values: int = 1 << 30) -> int:
+    """Host threads for generating `values` numbers: at most 16 (the cores
+    a GPU's share of the host has), at most one per 2^20 values (thread
+    start-up costs more than small fills)."""
     try:
         n = len(os.sched_getaffinity(0))
     except AttributeError:  # pragma: no cover
         n = os.cpu_count() or 1
-    return max(1, min(16, n))
+    return max(1, min(16, n, int(values) >> 20))
 
 
 # ----------------------------------------------------------------- host side
@@ -94,7 +97,7 @@ def host_f32(n: int, seed: int, tid: int, step: int, rank: int, i0: int, sigma: 
              outliers: bool = False, kind: int = KIND_NORMAL) -> np.ndarray:
     out = np.empty(int(n), dtype=np.float32)
     host_lib().zsg_host_fill_f32(out.ctypes.data, int(n), seed, tid, step, rank, int(i0),
-                                 float(sigma), int(outliers), int(kind), _threads())
+                                 float(sigma), int(outliers), int(kind), _threads(n))
     return out
 
 
@@ -102,7 +105,7 @@ def host_bf16(n: int, seed: int, tid: int, step: int, rank: int, i0: int, sigma:
               outliers: bool = False) -> np.ndarray:
     out = np.empty(int(n), dtype=np.uint16)
     host_lib().zsg_host_fill_bf16(out.ctypes.data, int(n), seed, tid, step, rank, int(i0),
-                                  float(sigma), int(outliers), _threads())
+                                  float(sigma), int(outliers), _threads(n))
     return out
 
 
@@ -111,7 +114,8 @@ def host_contrib(w: Workload, step: int, i0: int, n: int) -> np.ndarray:
     [i0, i0+n) at 1-based step `step`."""
     out = np.empty((w.n_d, int(n)), dtype=np.uint16)
     host_lib().zsg_host_fill_contrib(out.ctypes.data, w.n_d, int(n), int(n), w.seed, int(step),
-                                     int(i0), float(w.grad_sigma), int(w.outliers), _threads())
+                                     int(i0), float(w.grad_sigma), int(w.outliers),
+                                     _threads(w.n_d * int(n)))
     return out
 
 
@@ -126,7 +130,7 @@ def host_contrib_q8(w: Workload, step: int, i0: int, n: int) -> tuple[np.ndarray
     scales = np.empty((w.n_d, max(1, nb)), dtype=np.float32)
     host_lib().zsg_host_fill_contrib_q8(codes.ctypes.data, scales.ctypes.data, w.n_d, int(n),
                                         scales.shape[1], int(n), w.seed, int(step), int(i0),
-                                        blk, float(w.scale_sigma), _threads())
+                                        blk, float(w.scale_sigma), _threads(w.n_d * int(n)))
     return codes, scales[:, :nb]
 
 

@@ -150,11 +150,13 @@ class GpuShard:
 class OracleWindow:
     """Oracle state of shard elements [i0, i0+n) of workload w."""
 
-    def __init__(self, w: S.Workload, i0: int, n: int, threads: int = 16,
+    def __init__(self, w: S.Workload, i0: int, n: int, threads: int | None = None,
                  bias_correction: bool = True):
         import oracle
 
         self.O = oracle
+        if threads is None:  # one host thread per 2^18 elements, at most 16
+            threads = max(1, min(16, int(n) >> 18))
         self.w, self.i0, self.n, self.threads = w, int(i0), int(n), threads
         self.bias_correction = int(bool(bias_correction))
         self.master, self.m, self.v = S.host_state(w, i0, n)
