@@ -297,6 +297,13 @@ class OffloadShard:
     def free(self) -> None:
         if self.o is not None and self.o.value:
             rc = Z.zero_shard_offload_free(self.o)
+            self.o = None
             if rc:
                 raise Z.ZeroShardError(rc, "zero_shard_offload_free")
         self.o = None
+
+    def __del__(self):
+        try:
+            self.free()
+        except Exception:  # noqa: BLE001  (interpreter shutdown)
+            pass
