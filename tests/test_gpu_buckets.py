@@ -298,3 +298,22 @@ def test_arrival_delay_waits_and_bucketed_step_waits_for_it():
     _same(g1.host(), g2.host())
     g1.free()
     g2.free()
+
+
+def test_bucketed_sum_independent_of_stream_count():
+    """The bucketed S adds the bucket sums in bucket order, so it is the same
+    double whatever the number of worker streams, call after call."""
+    import torch
+
+    w = dataclasses.replace(S.by_name("13B-nd16-clip-int8"), max_norm=0.05)
+    n, bucket = 1_000_003, 65_536
+    g = GpuShard(w, n=n)
+    g.init_state()
+    g.fill_grads(1)
+    got = []
+    for streams in (1, 2, 3, 4, 2, 1):
+        g.shard.gnorm_bucketed(g.rows, bucket, g.sumsq, streams=streams)
+        torch.cuda.synchronize()
+        got.append(g.sumsq.cpu().numpy().view(np.uint64)[0])
+    assert len(set(got)) == 1, got
+    g.free()
