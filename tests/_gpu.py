@@ -273,9 +273,10 @@ class OffloadShard:
     def fill_grads(self, s: int) -> None:
         S.dev_contrib(self.w, s, self.rows_buf, self.n, self.stride)
 
-    def step(self, s: int, delayed: bool = True) -> None:
-        """Step s; without `delayed`, also wait for its host update."""
-        rc = Z.zero_shard_offload_step(self.o, self.tab, self.w.lr, self.w.t_of(s))
+    def step(self, s: int, delayed: bool = True, s_other: float = 0.0) -> None:
+        """Step s (s_other: the other shards' sum of squares); without
+        `delayed`, also wait for its host update."""
+        rc = Z.zero_shard_offload_step(self.o, self.tab, self.w.lr, self.w.t_of(s), s_other)
         if rc:
             raise Z.ZeroShardError(rc, "zero_shard_offload_step")
         if not delayed:

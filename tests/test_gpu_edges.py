@@ -494,3 +494,32 @@ def test_offload_delayed_parameters_and_errors():
     rc, _ = Z.zero_shard_offload_init(nod, bad, bad, threads=2)
     assert rc == Z.ZS_EINVAL
     g.free()
+
+
+def test_offload_with_other_shards_sum():
+    """With other ranks, S = S_local + S_other: the offloaded step given
+    S_other equals the on-device step clipped by the same global S."""
+    import torch
+
+    from tests._gpu import OffloadShard
+
+    w = _variant("13B-nd16-clip-int8", max_norm=0.05)
+    n, s_other = 200_003, 0.0123
+    g = GpuShard(w, n=n)
+    g.init_state()
+    off = OffloadShard(w, n=n, threads=4)
+    for s in (1, 2):
+        g.fill_grads(s)
+        off.fill_grads(s)
+        g.norm()
+        g.sumsq += s_other  # the all-reduced S
+        g.update(s)
+        off.step(s, s_other=s_other)
+    off.finish()
+    torch.cuda.synchronize()
+    got = g.host()
+    for name, host in (("master", off.master), ("m", off.m), ("v", off.v)):
+        assert np.array_equal(got[name].view(np.uint32), host.view(np.uint32)), name
+    assert np.array_equal(got["p"], off.params().cpu().numpy().view(np.uint16))
+    off.free()
+    g.free()
