@@ -20,7 +20,12 @@
  *          "DeepSpeed에서 쓰기" (gradient_clipping), "FSDP와의 관계"
  *          (reduce_dtype float32).
  * Where the pages leave a step open, the reading taken is stated at the
- * routine.
+ * routine.  Three such conventions are pinned only to the reading, not to
+ * anything the pages fix (parity unpinned by the pages): where eps enters
+ * Adam (after bias correction: the tests pin the closed forms of that
+ * reading), the clip constant 1e-6 with min(1, .) in orc_clip_coef, and the
+ * int8 scale convention (symmetric, absmax / 127, round half to even) of
+ * orc_quant_int8 and orc_dequant_bf16.
  */
 #ifndef ZS_ORACLE_H
 #define ZS_ORACLE_H
