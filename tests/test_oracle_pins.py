@@ -627,3 +627,163 @@ def test_dequant_is_two_roundings_of_the_exact_product():
         exact = Fraction(int(codes[i])) * Fraction(float(scales[i // block]))
         want = float(rne(rne(exact, 24), 8))
         assert _bf16_to_float(got[i:i + 1])[0] == want, i
+
+
+# ------------------------------- global clip across shards (S = S_local + S_other)
+
+def _dyadic_rows(nd: int, n: int, seed: int) -> list[np.ndarray]:
+    """bf16 rows of small integers times 2^-12 (|k| <= 255): every average is
+    exact in binary32, every square exact in binary64, and every partial sum
+    of squares over these lengths stays below 2^53 units of 2^-30, so the sum
+    of squares is exact in any order and any grouping."""
+    rng = np.random.default_rng(seed)
+    return [_bf16_bits(rng.integers(-255, 256, n).astype(np.float64) * 2.0**-12)
+            for _ in range(nd)]
+
+
+def _shard_bounds(n: int, nd: int, block: int) -> list[tuple[int, int]]:
+    per = -(-n // nd)
+    per = -(-per // block) * block
+    return [(r * per, min(n, (r + 1) * per)) for r in range(nd) if r * per < n]
+
+
+def _clipped_run(rows_of_step, n, h_of_step, nd_shards=None, s_other_scale=1.0, block=256):
+    """Three clipped steps of the whole vector (nd_shards None), or of each
+    shard separately with s_other = the other shards' summed S (times
+    s_other_scale, to show the test's sensitivity); returns the concatenated
+    master, m, v, bf16, codes and scales."""
+    master0, m0, v0 = (S.host_f32(n, 9, S.MASTER, 0, 0, 0, 0.02), np.zeros(n, np.float32),
+                       np.zeros(n, np.float32))
+    if nd_shards is None:
+        bounds = [(0, n)]
+    else:
+        bounds = _shard_bounds(n, nd_shards, block)
+    state = [(master0[lo:hi].copy(), m0[lo:hi].copy(), v0[lo:hi].copy()) for lo, hi in bounds]
+    outs = [None] * len(bounds)
+    for s in (1, 2, 3):
+        rows = rows_of_step(s)
+        # each shard's own S (the norm pass), then the scalar exchange
+        local = [O.gbar_sumsq([r[lo:hi] for r in rows])[1] for lo, hi in bounds]
+        for j, (lo, hi) in enumerate(bounds):
+            other = sum(x for i, x in enumerate(local) if i != j)
+            h = h_of_step(s)
+            h.s_other = other * s_other_scale
+            mst, mo, va = state[j]
+            outs[j] = O.step([r[lo:hi] for r in rows], mst, mo, va, h)
+    cat = lambda xs: np.concatenate(xs)  # noqa: E731
+    return (cat([x[0] for x in state]), cat([x[1] for x in state]), cat([x[2] for x in state]),
+            cat([o.p for o in outs]), cat([o.codes for o in outs]), cat([o.scales for o in outs]))
+
+
+def test_clipped_shard_concatenation_with_s_other_bitwise():
+    """Global clipping ("ZeRO (딥 러닝)", "DeepSpeed에서 쓰기": gradient_clipping)
+    scales every shard by the norm over ALL shards; elementwise independence
+    ("ZeRO-1") then lets the shards update apart.  Each shard adds the other
+    shards' sum of squares (s_other) to its own, and the concatenated shards
+    must equal the unpartitioned clipped step.  On dyadic contributions every
+    S is exact in any association, so the equality is bit for bit.  The clip
+    threshold lies above every shard's own norm and below the global norm:
+    dropping s_other leaves the shards unclipped, doubling it clips too hard,
+    and both are shown to break the equality."""
+    n, nd = 4 * 65536 + 3 * 256 + 40, 4
+    rows = {s: _dyadic_rows(4, n, 100 + s) for s in (1, 2, 3)}
+    g_norms = {s: np.sqrt(O.gbar_sumsq(rows[s])[1]) for s in rows}
+    local_max = max(np.sqrt(O.gbar_sumsq([r[lo:hi] for r in rows[s]])[1])
+                    for s in rows for lo, hi in _shard_bounds(n, nd, 256))
+    max_norm = float(np.float32(0.5 * (local_max + min(g_norms.values()))))
+    assert local_max < max_norm < min(g_norms.values())  # clip active only globally
+
+    def hyper(s):
+        return O.Hyper(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.1, t=s,
+                       max_norm=max_norm, quant_block=256)
+
+    whole = _clipped_run(rows.get, n, hyper)
+    parts = _clipped_run(rows.get, n, hyper, nd_shards=nd)
+    for name, a, b in zip(("master", "m", "v", "bf16", "codes", "scales"), whole, parts):
+        assert np.array_equal(a.view(np.uint8), b.view(np.uint8)), name
+    for scale in (0.0, 2.0):
+        wrong = _clipped_run(rows.get, n, hyper, nd_shards=nd, s_other_scale=scale)
+        assert not np.array_equal(wrong[1], whole[1]), scale  # m carries coef * gbar
+
+
+def test_clipped_shard_concatenation_seeded_within_one_ulp():
+    """The same on seeded N(0, 1e-3) contributions of the clipped 13B
+    workload: the shards' S is associated differently from the whole
+    vector's (the per-shard sums, then the exchange), so coef may differ in
+    its last binary64 bits, and every stored value within one ulp."""
+    w = S.by_name("13B-nd16-clip-int8")
+    n, nd = 3 * 65536 + 5000, 3
+    rows = {s: list(S.host_contrib(w, s, 0, n)) for s in (1, 2, 3)}
+    norm = min(np.sqrt(O.gbar_sumsq(rows[s])[1]) for s in rows)
+
+    def hyper(s):
+        return O.Hyper(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps,
+                       weight_decay=w.weight_decay, t=s, max_norm=float(np.float32(norm / 3)),
+                       quant_block=256)
+
+    whole = _clipped_run(rows.get, n, hyper)
+    parts = _clipped_run(rows.get, n, hyper, nd_shards=nd)
+    for name, a, b in zip(("master", "m", "v"), whole[:3], parts[:3]):
+        d = np.abs(a.view(np.int32).astype(np.int64) - b.view(np.int32).astype(np.int64))
+        assert d.max() <= 1, name
+    d = np.abs(whole[3].astype(np.int64) - parts[3].astype(np.int64))
+    assert d.max() <= 1
+
+
+def test_clip_sums_local_and_other_closed_form():
+    """All-equal averaged gradient c over n = 4^k elements split into shards:
+    S_local + S_other = n c^2 exactly, so every shard's coefficient is
+    max_norm / (|c| 2^k + 1e-6), and with m = 0 at t = 1 the stored momentum
+    is (1 - beta1) coef c.  A shard that ignored s_other would use its own
+    n_r c^2 instead and store a momentum 2x (n_r = n/4) larger."""
+    c, k, nd = 0.75, 8, 4
+    n = 4**k
+    rows = [np.full(n, _bf16_bits([c])[0], np.uint16) for _ in range(2)]
+    max_norm = 1.0
+    coef = max_norm / (abs(c) * 2**k + 1e-6)
+    b1 = float(np.float32(0.9))
+    per = n // nd
+    for r in range(nd):
+        lo, hi = r * per, (r + 1) * per
+        master = np.zeros(per, np.float32)
+        m = np.zeros(per, np.float32)
+        v = np.zeros(per, np.float32)
+        h = O.Hyper(lr=1e-3, t=1, max_norm=max_norm, s_other=(n - per) * c * c)
+        out = O.step([x[lo:hi] for x in rows], master, m, v, h)
+        assert out.sumsq == per * c * c
+        want = np.float32((1.0 - b1) * coef * c)
+        assert np.all(m == want), (r, m[0], want)
+
+
+# --------------------------------------------- Adam without bias correction
+
+def test_adam_no_bias_correction_closed_forms():
+    """bias_correction = 0: the moments are used as they are.  With a constant
+    gradient g from m = v = 0, m_T = (1 - b1^T) g and v_T = (1 - b2^T) g^2, so
+    step T moves theta by -lr (1 - b1^T) g / (sqrt(1 - b2^T) |g| + eps): at
+    t = 1 that is -lr (1 - b1) g / (sqrt(1 - b2) |g| + eps), about 3.2 lr for
+    (0.9, 0.999), against -lr g / (|g| + eps) when the corrections are
+    applied.  Checked per step for T = 1..6, and theta as the sum of the
+    steps."""
+    g = np.array([1e-3, -2e-4, 0.5, -7e-6, 3e-9, 0.0], np.float32)
+    theta0 = np.array([0.01, -0.02, 0.3, 1.0, -1e-5, 0.02], np.float32)
+    h = O.Hyper(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, bias_correction=0)
+    T = 6
+    hist, m, v = _adam_run([g] * T, theta0, h)
+    lr, b1, b2, eps = (float(np.float32(x)) for x in (1e-3, 0.9, 0.999, 1e-8))
+    g64 = g.astype(np.float64)
+    want = theta0.astype(np.float64)
+    for t, th in enumerate(hist, 1):
+        mt = (1.0 - b1**t) * g64
+        vt = (1.0 - b2**t) * g64 * g64
+        want = want - lr * mt / (np.sqrt(vt) + eps)
+        # theta carries one binary32 rounding per step
+        assert np.allclose(th, want, rtol=4e-7 * t, atol=1e-12), t
+    assert np.allclose(m, (1.0 - b1**T) * g64, rtol=1e-6, atol=0)
+    assert np.allclose(v, (1.0 - b2**T) * g64 * g64, rtol=1e-6, atol=0)
+    # the first step differs from the bias-corrected one by ~sqrt(1-b2)/(1-b1)
+    (c1,), _, _ = _adam_run([g], theta0, O.Hyper(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8))
+    (u1,), _, _ = _adam_run([g], theta0, h)
+    big = np.abs(g64) >= 1e-4  # eps negligible next to sqrt(1 - b2) |g|
+    ratio = (u1 - theta0).astype(np.float64)[big] / (c1 - theta0).astype(np.float64)[big]
+    assert np.allclose(ratio, (1 - b1) / np.sqrt(1 - b2), rtol=5e-3)
