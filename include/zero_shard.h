@@ -270,8 +270,12 @@ int zero_shard_host_step(const zs_desc *d, const float *gbar, float lr, int64_t 
  * names that buffer (NULL before any update has been uploaded).
  * zero_shard_offload_wait: finish the running host update and order
  * `stream` after its upload; zero_shard_offload_params then names the
- * newest parameters.  Errors of a host update are returned by the next
- * step or wait call.  zero_shard_offload_free waits and releases.
+ * newest parameters.  zero_shard_offload_init rejects a descriptor the host
+ * update would reject (geometry, beta, eps, weight decay, max_norm, block)
+ * before it allocates anything, and zero_shard_offload_step rejects a bad
+ * lr, t or s_other (negative or non-finite) before it queues anything; an
+ * error inside a running host update is returned by the next step or wait
+ * call.  zero_shard_offload_free waits and releases.
  * The results are those of zero_shard_step on the same inputs, bit for bit.
  * Errors: ZS_EINVAL, ZS_EALIGN, ZS_ENOMEM, ZS_EHIP, ZS_ESTATE. */
 typedef struct zs_offload zs_offload;

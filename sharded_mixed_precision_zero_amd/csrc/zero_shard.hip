@@ -34,6 +34,7 @@
 #include <unordered_set>
 
 #include "zero_shard.h"
+#include "zs_args.h"
 
 namespace {
 
@@ -487,6 +488,64 @@ __device__ __forceinline__ void step_vec(const StepArgs<Src> &A, int64_t vec, do
     if constexpr (QL > 0) quant_lane<QL>(p, nvalid, vec, A.codes, A.scales);
 }
 
+// The fp32 state of one full lane-vector: master, m, v, two 16-byte vectors
+// each.
+struct StateFrag {
+  f32x4 t[2], m[2], v[2];
+};
+
+template <bool NT, class Src>
+__device__ __forceinline__ void load_state(const StepArgs<Src> &A, int64_t vec, StateFrag &s) {
+  const f32x4 *t4 = reinterpret_cast<const f32x4 *>(A.master) + 2 * vec;
+  const f32x4 *m4 = reinterpret_cast<const f32x4 *>(A.m) + 2 * vec;
+  const f32x4 *v4 = reinterpret_cast<const f32x4 *>(A.v) + 2 * vec;
+  s.t[0] = ld<NT>(t4); s.t[1] = ld<NT>(t4 + 1);
+  s.m[0] = ld<NT>(m4); s.m[1] = ld<NT>(m4 + 1);
+  s.v[0] = ld<NT>(v4); s.v[1] = ld<NT>(v4 + 1);
+}
+
+// a2 (apply) + a3 + a4 (+ a5) on one full lane-vector whose averaged
+// gradient is g and whose state was loaded into s; every lane of the wave
+// calls it together when QL > 0.
+template <int QL, class Src>
+__device__ __forceinline__ void update_full(const StepArgs<Src> &A, int64_t vec, double coef,
+                                            const float (&g)[kVec], const StateFrag &s) {
+  constexpr bool nt = ZS_NT_STATE;
+  float th[kVec], mo[kVec], va[kVec], p[kVec];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    th[e] = s.t[0][e]; th[e + 4] = s.t[1][e];
+    mo[e] = s.m[0][e]; mo[e + 4] = s.m[1][e];
+    va[e] = s.v[0][e]; va[e + 4] = s.v[1][e];
+  }
+#pragma unroll
+  for (int e = 0; e < kVec; ++e) adam(coef * static_cast<double>(g[e]), th[e], mo[e], va[e], A.k);
+  unsigned pb[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    pb[e] = pack_bf16(th[2 * e], th[2 * e + 1]);
+    p[2 * e] = bf16_lo(pb[e]);
+    p[2 * e + 1] = bf16_hi(pb[e]);
+  }
+  f32x4 o[6];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    o[0][e] = th[e]; o[1][e] = th[e + 4];
+    o[2][e] = mo[e]; o[3][e] = mo[e + 4];
+    o[4][e] = va[e]; o[5][e] = va[e + 4];
+  }
+  f32x4 *t4 = reinterpret_cast<f32x4 *>(A.master) + 2 * vec;
+  f32x4 *m4 = reinterpret_cast<f32x4 *>(A.m) + 2 * vec;
+  f32x4 *v4 = reinterpret_cast<f32x4 *>(A.v) + 2 * vec;
+  st<nt>(o[0], t4); st<nt>(o[1], t4 + 1);
+  st<nt>(o[2], m4); st<nt>(o[3], m4 + 1);
+  st<nt>(o[4], v4); st<nt>(o[5], v4 + 1);
+  u32x4 pv;
+  pv.x = pb[0]; pv.y = pb[1]; pv.z = pb[2]; pv.w = pb[3];
+  st<kNtOut>(pv, reinterpret_cast<u32x4 *>(A.pout) + vec);
+  if constexpr (QL > 0) quant_lane<QL>(p, kVec, vec, A.codes, A.scales);
+}
+
 #ifndef ZS_WIDE_MIN_ROWS
 #define ZS_WIDE_MIN_ROWS 16
 #endif
@@ -522,42 +581,9 @@ __global__ void __launch_bounds__(kThreads) step_kernel(const StepArgs<Src> A) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t vec = wb + 64 * u + lane;
-      f32x4 *t4 = reinterpret_cast<f32x4 *>(A.master) + 2 * vec;
-      f32x4 *m4 = reinterpret_cast<f32x4 *>(A.m) + 2 * vec;
-      f32x4 *v4 = reinterpret_cast<f32x4 *>(A.v) + 2 * vec;
-      const f32x4 ta = ld<nt>(t4), tb = ld<nt>(t4 + 1), ma = ld<nt>(m4), mb = ld<nt>(m4 + 1),
-                  vx = ld<nt>(v4), vy = ld<nt>(v4 + 1);
-      float th[kVec], mo[kVec], va[kVec], p[kVec];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        th[e] = ta[e]; th[e + 4] = tb[e];
-        mo[e] = ma[e]; mo[e + 4] = mb[e];
-        va[e] = vx[e]; va[e + 4] = vy[e];
-      }
-#pragma unroll
-      for (int e = 0; e < kVec; ++e)
-        adam(coef * static_cast<double>(g[u][e]), th[e], mo[e], va[e], A.k);
-      unsigned pb[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        pb[e] = pack_bf16(th[2 * e], th[2 * e + 1]);
-        p[2 * e] = bf16_lo(pb[e]);
-        p[2 * e + 1] = bf16_hi(pb[e]);
-      }
-      f32x4 o[6];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        o[0][e] = th[e]; o[1][e] = th[e + 4];
-        o[2][e] = mo[e]; o[3][e] = mo[e + 4];
-        o[4][e] = va[e]; o[5][e] = va[e + 4];
-      }
-      st<nt>(o[0], t4); st<nt>(o[1], t4 + 1);
-      st<nt>(o[2], m4); st<nt>(o[3], m4 + 1);
-      st<nt>(o[4], v4); st<nt>(o[5], v4 + 1);
-      u32x4 pv;
-      pv.x = pb[0]; pv.y = pb[1]; pv.z = pb[2]; pv.w = pb[3];
-      st<kNtOut>(pv, reinterpret_cast<u32x4 *>(A.pout) + vec);
-      if constexpr (QL > 0) quant_lane<QL>(p, kVec, vec, A.codes, A.scales);
+      StateFrag sf;
+      load_state<nt>(A, vec, sf);
+      update_full<QL>(A, vec, coef, g[u], sf);
     }
   }
 }
@@ -839,8 +865,6 @@ bool live(zs_handle *h) {
 
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-bool is_finite(double x) { return std::isfinite(x); }
-
 int quant_lanes(int32_t block) {
   switch (block) {
     case 32: return 4;
@@ -1008,7 +1032,7 @@ int step_args_ok(zs_handle *h, float lr, int64_t t, const double *global_sumsq_d
   if (!live(h)) return ZS_ESTATE;
   const zs_desc &d = h->d;
   if (d.shard_len > 0 && !d.master) return ZS_EINVAL;  // norm-only handle
-  if (!(lr >= 0.0f) || !is_finite(lr) || t < 1) return ZS_EINVAL;
+  if (!zs_args::step_ok(lr, t)) return ZS_EINVAL;
   const bool clip = d.max_norm > 0.0f;
   if (clip && !global_sumsq_dev) return ZS_EINVAL;
   if (clip && !aligned(global_sumsq_dev, 8)) return ZS_EALIGN;
@@ -1263,17 +1287,7 @@ const char *zero_shard_strerror(int code) {
 int zero_shard_init(const zs_desc *d, zs_handle **out) {
   if (!d || !out) return ZS_EINVAL;
   *out = nullptr;
-  if (d->n_d < 1 || d->n_d > ZS_MAX_ND || d->r < 0 || d->r >= d->n_d || d->phi < 0)
-    return ZS_EINVAL;
-  const int64_t want = zero_shard_len(d->phi, d->n_d, d->r);
-  if (!(d->shard_len == want || (d->r == 0 && d->shard_len == d->phi))) return ZS_EINVAL;
-  if (!(d->beta1 >= 0.0f && d->beta1 < 1.0f && d->beta2 >= 0.0f && d->beta2 < 1.0f))
-    return ZS_EINVAL;
-  if (!(d->eps > 0.0f) || !is_finite(d->eps)) return ZS_EINVAL;
-  if (!(d->weight_decay >= 0.0f) || !is_finite(d->weight_decay)) return ZS_EINVAL;
-  if (d->bias_correction != 0 && d->bias_correction != 1) return ZS_EINVAL;
-  if (!is_finite(d->max_norm)) return ZS_EINVAL;
-  if (d->quant_block != 0 && quant_lanes(d->quant_block) < 0) return ZS_EINVAL;
+  if (!zs_args::geometry_ok(*d) || !zs_args::hyper_ok(*d)) return ZS_EINVAL;
   const int64_t n = d->shard_len;
   if (n > 0) {
     // state and output: all four, or none (a norm-only handle, e.g. for an

@@ -27,6 +27,7 @@
 #include <vector>
 
 #include "zero_shard.h"
+#include "zs_args.h"
 
 namespace {
 
@@ -132,8 +133,6 @@ bool have_avx512() {
   return yes;
 }
 
-bool finite_pos(float x) { return std::isfinite(x) && x > 0.0f; }
-
 }  // namespace
 
 // Partition geometry (declared in include/zero_shard.h): ceil(phi / n_d)
@@ -149,19 +148,9 @@ extern "C" int64_t zero_shard_len(int64_t phi, int32_t n_d, int32_t r) {
 extern "C" int zero_shard_host_step(const zs_desc *d, const float *gbar, float lr, int64_t t,
                                     double global_sumsq, int32_t threads) {
   if (!d) return ZS_EINVAL;
-  if (d->n_d < 1 || d->n_d > ZS_MAX_ND || d->r < 0 || d->r >= d->n_d || d->phi < 0)
+  if (!zs_args::geometry_ok(*d) || !zs_args::hyper_ok(*d) || !zs_args::step_ok(lr, t))
     return ZS_EINVAL;
-  const int64_t want = zero_shard_len(d->phi, d->n_d, d->r);
-  if (!(d->shard_len == want || (d->r == 0 && d->shard_len == d->phi))) return ZS_EINVAL;
-  if (!(d->beta1 >= 0.0f && d->beta1 < 1.0f && d->beta2 >= 0.0f && d->beta2 < 1.0f))
-    return ZS_EINVAL;
-  if (!finite_pos(d->eps) || !(d->weight_decay >= 0.0f) || !std::isfinite(d->weight_decay))
-    return ZS_EINVAL;
-  if (d->bias_correction != 0 && d->bias_correction != 1) return ZS_EINVAL;
-  if (!std::isfinite(d->max_norm)) return ZS_EINVAL;
   const int32_t qb = d->quant_block;
-  if (qb != 0 && qb != 32 && qb != 64 && qb != 128 && qb != 256 && qb != 512) return ZS_EINVAL;
-  if (!(lr >= 0.0f) || !std::isfinite(lr) || t < 1) return ZS_EINVAL;
   const int64_t n = d->shard_len;
   if (n == 0) return ZS_OK;
   if (!gbar || !d->master || !d->m || !d->v || !d->param_out) return ZS_EINVAL;

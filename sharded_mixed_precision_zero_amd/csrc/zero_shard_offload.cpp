@@ -26,6 +26,7 @@
 
 #include <hip/hip_runtime_api.h>
 
+#include <cmath>
 #include <cstdint>
 #include <cstring>
 #include <mutex>
@@ -34,6 +35,7 @@
 #include <unordered_set>
 
 #include "zero_shard.h"
+#include "zs_args.h"
 
 struct zs_offload {
   uint32_t magic;
@@ -122,7 +124,8 @@ int zero_shard_offload_init(const zs_desc *host, zs_bf16 *param_dev0, zs_bf16 *p
   if (!host || !out || threads < 1) return ZS_EINVAL;
   *out = nullptr;
   const int64_t n = host->shard_len;
-  if (n < 0 || zero_shard_len(host->phi, host->n_d, host->r) < 0) return ZS_EINVAL;
+  // everything the host update will check, before anything is allocated
+  if (!zs_args::geometry_ok(*host) || !zs_args::hyper_ok(*host)) return ZS_EINVAL;
   if (n > 0 && (!host->master || !host->m || !host->v || !param_dev0 || !param_dev1))
     return ZS_EINVAL;
   if (n > 0 && host->quant_block && (!host->q_codes || !host->q_scales)) return ZS_EINVAL;
@@ -189,7 +192,8 @@ int zero_shard_offload_init(const zs_desc *host, zs_bf16 *param_dev0, zs_bf16 *p
 int zero_shard_offload_step(zs_offload *o, const zs_bf16 *const *contrib, float lr, int64_t t,
                             double s_other) {
   if (!live(o)) return ZS_ESTATE;
-  if (!(lr >= 0.0f) || t < 1 || s_other != s_other || s_other < 0.0) return ZS_EINVAL;
+  // everything the host update will check, before anything is queued
+  if (!zs_args::step_ok(lr, t) || !(s_other >= 0.0) || !std::isfinite(s_other)) return ZS_EINVAL;
   const int k = int(o->steps & 1), prev = k ^ 1;
   // the spill of the previous step has left the device before it is rewritten
   if (hipStreamWaitEvent(o->compute, o->copied[prev], 0) != hipSuccess) return ZS_EHIP;

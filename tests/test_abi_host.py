@@ -168,3 +168,36 @@ def test_dequant_rejects_bad_arguments(args, code):
     st = (ctypes.c_void_p * 4)(*a["scales"])
     rc = Z._lib.zero_shard_dequant(ct, st, a["n_d"], a["phi"], a["block"], a["out"], None)
     assert rc == code
+
+
+def test_offload_init_rejects_bad_hyperparameters_before_allocating():
+    """zero_shard_offload_init checks everything the host update will check
+    (partition geometry, beta in [0, 1), eps > 0, weight decay >= 0, all
+    finite) before it allocates or touches a device, so a bad descriptor is
+    ZS_EINVAL from this call and not an error of a later step.  (Device
+    pointers here are never dereferenced.)"""
+    import numpy as np
+
+    n = 1000
+    master, m, v = (np.zeros(n, np.float32) for _ in range(3))
+    fake_dev = ctypes.c_void_p(1 << 20)  # 16-byte aligned, never used
+
+    def init(**kw):
+        hyper = dict(beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0)
+        geo = dict(phi=n, n_d=1, r=0, shard_len=n)
+        for k in list(kw):
+            if k in hyper:
+                hyper[k] = kw.pop(k)
+            elif k in geo:
+                geo[k] = kw.pop(k)
+        d = Z.host_desc(master=master, m=m, v=v, param_out=None, **geo, **hyper)
+        o = ctypes.c_void_p()
+        return Z._lib.zero_shard_offload_init(ctypes.byref(d), fake_dev, fake_dev, None, 2,
+                                              ctypes.byref(o)), o
+
+    for bad in (dict(beta1=1.0), dict(beta1=-0.5), dict(beta2=1.0), dict(eps=0.0),
+                dict(eps=-1e-8), dict(eps=float("inf")), dict(weight_decay=-0.1),
+                dict(weight_decay=float("nan")), dict(shard_len=n - 1),
+                dict(phi=n, n_d=2, r=2), dict(phi=n, n_d=2, r=1, shard_len=n)):
+        rc, o = init(**bad)
+        assert rc == Z.ZS_EINVAL and not o.value, bad

@@ -474,10 +474,32 @@ def test_offload_delayed_parameters_and_errors():
     off.finish()
     assert np.array_equal(off.params().cpu().numpy().view(np.uint16), seen[3])
     o = off.o
+    # rejected by the call itself, before anything is queued: the pipeline
+    # is untouched and the next valid step (and wait) reports no error
     assert Z.zero_shard_offload_step(o, off.tab, -1.0, 4) == Z.ZS_EINVAL
+    assert Z.zero_shard_offload_step(o, off.tab, float("inf"), 4) == Z.ZS_EINVAL
+    assert Z.zero_shard_offload_step(o, off.tab, float("nan"), 4) == Z.ZS_EINVAL
     assert Z.zero_shard_offload_step(o, off.tab, 1e-3, 0) == Z.ZS_EINVAL
     assert Z.zero_shard_offload_step(o, off.tab, 1e-3, 4, float("nan")) == Z.ZS_EINVAL
+    assert Z.zero_shard_offload_step(o, off.tab, 1e-3, 4, float("inf")) == Z.ZS_EINVAL
+    assert Z.zero_shard_offload_step(o, off.tab, 1e-3, 4, -1.0) == Z.ZS_EINVAL
     assert Z.zero_shard_offload_step(o, None, 1e-3, 4) == Z.ZS_EINVAL
+    assert np.array_equal(off.params().cpu().numpy().view(np.uint16), seen[3])
+    g.fill_grads(4)
+    g.step(4)
+    off.fill_grads(4)
+    off.step(4)
+    off.finish()
+    assert np.array_equal(off.params().cpu().numpy().view(np.uint16), g.host()["p"])
+    for bad_h in (dict(beta1=1.0), dict(beta2=-0.1), dict(eps=0.0), dict(eps=float("inf")),
+                  dict(weight_decay=-0.1), dict(weight_decay=float("nan"))):
+        hd = dict(beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=w.weight_decay)
+        hd.update(bad_h)
+        desc_bad = Z.host_desc(phi=n, n_d=w.n_d, r=0, shard_len=n, master=off.master, m=off.m,
+                               v=off.v, param_out=None, **hd)
+        pb = torch.empty(n, dtype=torch.int16, device="cuda")
+        rc, ob = Z.zero_shard_offload_init(desc_bad, pb, pb, threads=2)
+        assert rc == Z.ZS_EINVAL and not ob, bad_h
     off.free()
     assert Z.zero_shard_offload_step(o, off.tab, 1e-3, 4) == Z.ZS_ESTATE
     assert Z.zero_shard_offload_wait(o) == Z.ZS_ESTATE
