@@ -317,3 +317,76 @@ def test_bucketed_sum_independent_of_stream_count():
         got.append(g.sumsq.cpu().numpy().view(np.uint64)[0])
     assert len(set(got)) == 1, got
     g.free()
+
+
+@pytest.mark.parametrize("contrib,clip,bucket,streams", [
+    ("bf16", 0.05, 65_536, 2),    # ragged last bucket (300,001 = 4 x 65,536 + 37,857)
+    ("bf16", 0.05, 512 * 37, 3),
+    ("bf16", 0.0, 65_536, 2),
+    ("q8", 0.05, 65_536, 2),
+    ("q8", 0.05, 131_072, 4),
+    ("q8", 0.0, 512 * 37, 3),
+])
+def test_bucketed_against_oracle(contrib, clip, bucket, streams):
+    """The bucketed step's outputs against the oracle directly, element by
+    element, at every step: master, m, v within the fp32 tolerance, bf16
+    within 1 ulp, int8 codes and scales exact (on the GPU's own bf16, and on
+    every block whose bf16 input equals the oracle's).  With clipping the
+    oracle takes its own S over the whole shard; the GPU's bucketed S is
+    checked against it within the bound for the two summation orders.  This
+    pins the bucket offsets (rows, scales of int8 contributions, int8 output
+    scales) and the ragged last bucket to the definition, not to the
+    unbucketed kernel."""
+    import torch
+
+    if contrib == "bf16":
+        w = dataclasses.replace(S.by_name("13B-nd16-clip-int8"), max_norm=clip)
+    else:
+        w = dataclasses.replace(S.by_name("7.5B-nd64-zeropp"), n_d=16, max_norm=clip,
+                                weight_decay=0.1, warm=False, t0=0)
+    n, cb = 300_001, w.contrib_block
+    log(f"case bucketed vs oracle {contrib} clip={clip} bucket={bucket} streams={streams}")
+    g = GpuShard(w, n=n)
+    g.init_state()
+    master, m, v = S.host_state(w, 0, n)
+    for s in range(1, 4):
+        g.fill_grads(s)
+        if cb:
+            codes, scales = S.host_contrib_q8(w, s, 0, n)
+            if clip > 0:
+                g.shard.gnorm_bucketed_q8(g.qrows, g.srows, cb, bucket, g.sumsq,
+                                          streams=streams)
+                g.shard.step_bucketed_q8(None, None, cb, bucket, w.lr, w.t_of(s), g.sumsq,
+                                         streams=streams)
+            else:
+                g.shard.step_bucketed_q8(g.qrows, g.srows, cb, bucket, w.lr, w.t_of(s),
+                                         streams=streams)
+        else:
+            rows = list(S.host_contrib(w, s, 0, n))
+            if clip > 0:
+                g.shard.gnorm_bucketed(g.rows, bucket, g.sumsq, streams=streams)
+                g.shard.step_bucketed(None, bucket, w.lr, w.t_of(s), g.sumsq, streams=streams)
+            else:
+                g.shard.step_bucketed(g.rows, bucket, w.lr, w.t_of(s), streams=streams)
+        h = O.Hyper(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps,
+                    weight_decay=w.weight_decay, t=w.t_of(s), max_norm=clip,
+                    quant_block=w.quant_block)
+        out = (O.step_q8(list(codes), list(scales), cb, master, m, v, h, threads=4) if cb
+               else O.step(rows, master, m, v, h, threads=4))
+        torch.cuda.synchronize()
+        if clip > 0:
+            s_gpu = float(g.sumsq.item())
+            tol = P.sumsq_tolerance(n, out.sumsq, buckets=-(-n // bucket))
+            assert abs(s_gpu - out.sumsq) <= tol, (s_gpu, out.sumsq, tol)
+        got = g.host()
+        name = f"bucketed {contrib} step {s}"
+        P.f32_close(f"{name} master", got["master"], master)
+        P.f32_close(f"{name} m", got["m"], m)
+        P.f32_close(f"{name} v", got["v"], v)
+        P.bf16_close(f"{name} bf16", got["p"], out.p)
+        c_own, s_own = O.quant_int8(got["p"], w.quant_block)
+        assert np.array_equal(got["codes"], c_own) and np.array_equal(
+            got["scales"].view(np.uint32), s_own.view(np.uint32)), name
+        P.int8_exact(f"{name} int8", got["codes"], got["scales"], out.codes, out.scales,
+                     got["p"], out.p, w.quant_block)
+    g.free()

@@ -4,7 +4,10 @@ elements on 2 worker streams; offload with 16 host threads and the one-step
 delayed update).  Both are scheduling variants of the same definition, so
 their outputs are compared with the on-device unbucketed step over the
 whole shard (bit for bit, given the same S), and the bucketed S with the
-unbucketed S within the bound for two binary64 summation orders."""
+unbucketed S within the bound for two binary64 summation orders.  The
+bucketed outputs are also compared with the oracle directly on windows
+across bucket boundaries (the head, the tail, the first boundaries, one in
+the middle, the last), clipped by the oracle's own S."""
 
 from __future__ import annotations
 
@@ -12,8 +15,9 @@ import numpy as np
 import pytest
 
 import seeded_inputs as S
+import oracle as O
 from tests import _parity as P
-from tests._gpu import GpuShard, OffloadShard, log
+from tests._gpu import GpuShard, OffloadShard, OracleWindow, log, oracle_global_sumsq
 
 pytestmark = pytest.mark.gpu
 
@@ -56,6 +60,12 @@ def test_bucketed_full_size(name):
     a, b = GpuShard(w), GpuShard(w)
     a.init_state()
     b.init_state()
+    n, nb = w.shard_len, -(-w.shard_len // bl)
+    half = 8192  # windows straddle bucket boundaries by this much on each side
+    cuts = sorted({1, 2, nb // 2, nb - 1})
+    wins = [(0, 2 * half)] + [(j * bl - half, j * bl + half) for j in cuts if 0 < j < nb]
+    wins.append(((n - 2 * half) // 256 * 256, n))
+    ows = [OracleWindow(w, lo, hi - lo) for lo, hi in wins]
     for s in range(1, 3):
         a.fill_grads(s)
         b.fill_grads(s)
@@ -74,7 +84,26 @@ def test_bucketed_full_size(name):
             b.shard.step_bucketed(b.rows, bl, w.lr, w.t_of(s), streams=2)
         torch.cuda.synchronize()
         _dev_equal(a, b)
-        log(f"  step {s}: bitwise equal")
+        s_orc = oracle_global_sumsq(w, s) if w.max_norm > 0 else None
+        if s_orc is not None:
+            sb = float(b.sumsq.item())
+            tol = P.sumsq_tolerance(n, s_orc, buckets=nb)
+            assert abs(sb - s_orc) <= tol, (sb, s_orc, tol)
+        for (lo, hi), ow in zip(wins, ows):
+            o = ow.step(s, sumsq_total=s_orc)
+            got = b.host(lo, hi)
+            nm = f"{name} bucketed step {s} [{lo},{hi})"
+            P.f32_close(f"{nm} master", got["master"], ow.master)
+            P.f32_close(f"{nm} m", got["m"], ow.m)
+            P.f32_close(f"{nm} v", got["v"], ow.v)
+            P.bf16_close(f"{nm} bf16", got["p"], o.p)
+            if w.quant_block:
+                c_own, _ = O.quant_int8(got["p"], w.quant_block)
+                assert np.array_equal(got["codes"], c_own), nm
+                P.int8_exact(f"{nm} int8", got["codes"], got["scales"], o.codes, o.scales,
+                             got["p"], o.p, w.quant_block)
+        log(f"  step {s}: bitwise equal to the unbucketed step; {len(wins)} windows across "
+            f"bucket boundaries within tolerance of the oracle")
     a.free()
     b.free()
 

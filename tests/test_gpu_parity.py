@@ -5,7 +5,8 @@ Tolerances (tests/_parity.py): fp32 master/m/v within 1e-9 + 2e-6|x|,
 bf16 within 1 ulp, int8 codes and scales exact on identical bf16 input.
 Small workloads are compared in full at every step; the full-size ones (in
 the launch configuration the benchmark times) on windows the oracle
-evolves element by element, plus the global norm over the whole shard.
+evolves element by element, compared at every step of the workload, plus
+the global norm over the whole shard at every clipped step.
 """
 
 from __future__ import annotations
@@ -44,6 +45,12 @@ def _compare(name, g: dict, o: O.StepOut, ow: OracleWindow, block: int = 0) -> d
         diff = P.int8_exact(f"{name} int8", g["codes"], g["scales"], o.codes, o.scales,
                             g["p"], o.p, block)
         st["int8_blocks_with_differing_input"] = int(diff.sum())
+        # every block, those with differing input included: the GPU's codes
+        # and scales are the quantizer's of the GPU's own bf16
+        c_own, s_own = O.quant_int8(g["p"], block)
+        assert np.array_equal(g["codes"], c_own), f"{name} int8 codes vs own bf16"
+        assert np.array_equal(g["scales"].view(np.uint32), s_own.view(np.uint32)), \
+            f"{name} int8 scales vs own bf16"
     return st
 
 
@@ -111,8 +118,7 @@ def test_gpt2_small_full_then_windows():
         else:
             for (lo, hi), ow in zip(wins, ows):
                 o = ow.step(s)
-                if s % 10 == 0 or s == w.steps:
-                    _compare(f"{w.name} step {s} [{lo},{hi})", g.host(lo, hi), o, ow)
+                _compare(f"{w.name} step {s} [{lo},{hi})", g.host(lo, hi), o, ow)
     g.free()
 
 
@@ -129,8 +135,7 @@ def test_7p5b_nd64_windows():
         g.step(s)
         for (lo, hi), ow in zip(wins, ows):
             o = ow.step(s)
-            if s in (1, 2, 10, 25) or s == w.steps:
-                _compare(f"{w.name} step {s} [{lo},{hi})", g.host(lo, hi), o, ow)
+            _compare(f"{w.name} step {s} [{lo},{hi})", g.host(lo, hi), o, ow)
     g.free()
 
 
@@ -149,19 +154,19 @@ def test_7p5b_zeropp_windows():
         g.step(s)
         for (lo, hi), ow in zip(wins, ows):
             o = ow.step(s)
-            if s in (1, 2, 10, 25) or s == w.steps:
-                _compare(f"{w.name} step {s} [{lo},{hi})", g.host(lo, hi), o, ow, w.quant_block)
+            _compare(f"{w.name} step {s} [{lo},{hi})", g.host(lo, hi), o, ow, w.quant_block)
     g.free()
 
 
 def test_13b_clip_int8_full_norm_and_windows():
     """Clipped steps need the norm of the whole averaged gradient: the oracle
-    streams all 16 x 812.5M contributions through the host for each step."""
+    streams all 16 x 812.5M contributions through the host for each of the
+    workload's 10 steps; S and every window are compared at every step."""
     import torch
 
     w = S.by_name("13B-nd16-clip-int8")
     n = w.shard_len
-    steps = 2
+    steps = w.steps
     log(f"case {w.name}: n={n} n_d={w.n_d} steps={steps} clip={w.max_norm} block={w.quant_block}")
     g = GpuShard(w)
     g.init_state()
@@ -200,8 +205,7 @@ def test_13b_stage0_nd1_windows():
         g.step(s)
         for (lo, hi), ow in zip(wins, ows):
             o = ow.step(s)
-            if s in (1, 5) or s == w.steps:
-                _compare(f"{w.name} step {s} [{lo},{hi})", g.host(lo, hi), o, ow)
+            _compare(f"{w.name} step {s} [{lo},{hi})", g.host(lo, hi), o, ow)
     g.free()
 
 
