@@ -78,8 +78,10 @@ typedef enum zs_status {
   ZS_ENOMEM = -3,  /* the library's own scratch could not be allocated     */
   ZS_EHIP = -4,    /* a HIP runtime call or kernel launch failed           */
   ZS_EDEVICE = -5, /* the current device is not gfx950                     */
-  ZS_ESTATE = -6   /* call out of order (step reading a gradient spill
+  ZS_ESTATE = -6,  /* call out of order (step reading a gradient spill
                       that no norm pass has written) or a dead handle      */
+  ZS_ETOOBIG = -7  /* shard longer than zero_shard_gnorm_noalloc's static
+                      scratch allows                                       */
 } zs_status;
 
 #define ZS_MAX_ND 64 /* most contributions one call can average */
@@ -131,6 +133,24 @@ int zero_shard_init(const zs_desc *d, zs_handle **out);
  * the S that zero_shard_step takes.  Errors: ZS_EINVAL, ZS_EALIGN, ZS_EHIP,
  * ZS_ESTATE. */
 int zero_shard_gnorm(zs_handle *h, const zs_bf16 *const *contrib, double *sumsq_dev);
+
+/* zero_shard_gnorm for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same sum of squares S_local and the same spill (when
+ * d->gbar_ws is set), bit for bit, without a handle.  Takes the descriptor
+ * itself (d->n_d, d->shard_len, d->gbar_ws and d->stream are used; the
+ * state pointers and hyper-parameters are ignored), contrib and sumsq_dev as
+ * for zero_shard_gnorm.  It allocates nothing: the block partials live in a
+ * static device array of the library (512 KiB on each GPU the library runs
+ * on, kept until the process ends), which bounds the shard at one partial
+ * per 16384 elements, 65536 partials: shard_len <= 2^30 (ZS_ETOOBIG
+ * beyond).  Every call on one GPU uses that GPU's one array: calls that
+ * overlap on one GPU (other streams, other threads) race and must be
+ * ordered by the caller; the partials need no clearing (each call writes
+ * all it reads).  Queues two kernel launches on d->stream and nothing else.
+ * Errors: ZS_EINVAL, ZS_EALIGN, ZS_ETOOBIG, ZS_EDEVICE, ZS_EHIP. */
+int zero_shard_gnorm_noalloc(const zs_desc *d, const zs_bf16 *const *contrib,
+                             double *sumsq_dev);
 
 /* a1 + a3 + a4 (+ a5 when quant_block > 0): one optimizer step at 1-based
  * step counter t with learning rate lr >= 0.  contrib as for gnorm; it may

@@ -17,7 +17,8 @@ import os
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libzeroshard.so")
 
-ZS_OK, ZS_EINVAL, ZS_EALIGN, ZS_ENOMEM, ZS_EHIP, ZS_EDEVICE, ZS_ESTATE = 0, -1, -2, -3, -4, -5, -6
+ZS_OK, ZS_EINVAL, ZS_EALIGN, ZS_ENOMEM, ZS_EHIP, ZS_EDEVICE, ZS_ESTATE, ZS_ETOOBIG = (
+    0, -1, -2, -3, -4, -5, -6, -7)
 ZS_MAX_ND = 64
 QUANT_BLOCKS = (32, 64, 128, 256, 512)
 
@@ -62,6 +63,9 @@ _lib.zero_shard_init.restype = ctypes.c_int
 _lib.zero_shard_init.argtypes = [ctypes.POINTER(zs_desc), ctypes.POINTER(_handle_p)]
 _lib.zero_shard_gnorm.restype = ctypes.c_int
 _lib.zero_shard_gnorm.argtypes = [_handle_p, ctypes.c_void_p, ctypes.c_void_p]
+_lib.zero_shard_gnorm_noalloc.restype = ctypes.c_int
+_lib.zero_shard_gnorm_noalloc.argtypes = [ctypes.POINTER(zs_desc), ctypes.c_void_p,
+                                          ctypes.c_void_p]
 _lib.zero_shard_step.restype = ctypes.c_int
 _lib.zero_shard_step.argtypes = [_handle_p, ctypes.c_void_p, ctypes.c_float, ctypes.c_int64,
                                  ctypes.c_void_p]
@@ -116,7 +120,8 @@ _lib.zero_shard_strerror.argtypes = [ctypes.c_int]
 _lib.zero_shard_len.restype = ctypes.c_int64
 _lib.zero_shard_len.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32]
 
-EXPORTS = ("zero_shard_init", "zero_shard_gnorm", "zero_shard_step", "zero_shard_gnorm_q8",
+EXPORTS = ("zero_shard_init", "zero_shard_gnorm", "zero_shard_gnorm_noalloc", "zero_shard_step",
+           "zero_shard_gnorm_q8",
            "zero_shard_step_q8", "zero_shard_gnorm_bucketed", "zero_shard_step_bucketed",
            "zero_shard_gnorm_bucketed_q8", "zero_shard_step_bucketed_q8",
            "zero_shard_quant", "zero_shard_dequant",
@@ -176,6 +181,13 @@ def zero_shard_init(desc: zs_desc) -> tuple[int, ctypes.c_void_p]:
 
 def zero_shard_gnorm(h, contrib, sumsq_dev) -> int:
     return _lib.zero_shard_gnorm(h, contrib_table(contrib), _ptr(sumsq_dev))
+
+
+def zero_shard_gnorm_noalloc(desc: zs_desc, contrib, sumsq_dev) -> int:
+    """zero_shard_gnorm without a handle and without allocating (desc: a
+    zs_desc; its n_d, shard_len, gbar_ws and stream are used)."""
+    return _lib.zero_shard_gnorm_noalloc(ctypes.byref(desc), contrib_table(contrib),
+                                         _ptr(sumsq_dev))
 
 
 def zero_shard_step(h, contrib, lr: float, t: int, global_sumsq_dev=None) -> int:

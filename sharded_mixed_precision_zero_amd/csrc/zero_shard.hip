@@ -832,6 +832,36 @@ constexpr uint32_t kMagic = 0x5a534831u;
 
 }  // namespace
 
+// The block partials of the allocation-free norm pass
+// (zero_shard_gnorm_noalloc): a device array of the library itself, one copy
+// on every GPU the library runs on, held until the process ends.  Host code
+// never names it for its memory: it uses the device address that
+// hipGetSymbolAddress returns for the current GPU (scratch_address below).
+constexpr int64_t kStaticPartials = 65536;  // 512 KiB: shards up to 2^30 bf16-row elements
+static __device__ __align__(256) double scratch[kStaticPartials];
+
+namespace {
+
+std::mutex g_scratch_mu;
+double *g_scratch_dev[64] = {};  // device address of `scratch` per device ordinal
+
+// This GPU's copy of `scratch`, resolved once per device with that device
+// current (at zero_shard_init, or at the first allocation-free call).
+int scratch_address(double **out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return ZS_EDEVICE;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return ZS_EHIP;
+    g_scratch_dev[dev] = static_cast<double *>(p);
+  }
+  *out = g_scratch_dev[dev];
+  return ZS_OK;
+}
+
+}  // namespace
+
 constexpr int kMaxBucketStreams = 4;  // worker streams of the bucketed calls
 constexpr int64_t kBucketAlign = 512;  // bucket lengths are multiples of this
 
@@ -941,9 +971,9 @@ Q8Rows shifted(const Q8Rows &s, int nd, int64_t off) {
   return r;
 }
 
-int check_rows(const zs_handle *h, const zs_bf16 *const *contrib, Bf16Rows *src) {
+int check_rows(int nd, const zs_bf16 *const *contrib, Bf16Rows *src) {
   if (!contrib) return ZS_EINVAL;
-  for (int k = 0; k < h->d.n_d; ++k) {
+  for (int k = 0; k < nd; ++k) {
     if (!contrib[k]) return ZS_EINVAL;
     if (!aligned(contrib[k], 16)) return ZS_EALIGN;
     src->p[k] = reinterpret_cast<const u32x4 *>(contrib[k]);
@@ -999,15 +1029,15 @@ int gnorm_args_ok(zs_handle *h, double *sumsq_dev) {
 // a2, first sweep over one part, after the contributions were checked:
 // block partials, then the fixed-order final reduction into *sumsq_dev.
 template <class Src>
-int launch_gnorm(zs_handle *h, const Src &src, const Part &part, double *sumsq_dev) {
+int launch_gnorm(int nd, float *gbar_ws, const Src &src, const Part &part, double *sumsq_dev) {
   const int64_t n = part.len;
   const hipStream_t st = part.st;
   const int64_t blocks = norm_blocks<Src>(n);
   NormArgs<Src> A;
-  A.src = n > 0 ? shifted(src, h->d.n_d, part.off) : src;
-  A.avg = make_avg(h->d.n_d);
+  A.src = n > 0 ? shifted(src, nd, part.off) : src;
+  A.avg = make_avg(nd);
   A.n = n;
-  A.gbar_out = h->d.gbar_ws ? h->d.gbar_ws + part.off : nullptr;
+  A.gbar_out = gbar_ws ? gbar_ws + part.off : nullptr;
   A.partials = part.partials;
   hipLaunchKernelGGL(gnorm_partial_kernel<Src>, dim3(unsigned(blocks)), dim3(kThreads), 0, st,
                      A);
@@ -1022,7 +1052,7 @@ template <class Src>
 int run_gnorm(zs_handle *h, const Src &src, double *sumsq_dev) {
   int rc = current_device_ok(h);
   if (rc) return rc;
-  if ((rc = launch_gnorm(h, src, whole(h), sumsq_dev))) return rc;
+  if ((rc = launch_gnorm(h->d.n_d, h->d.gbar_ws, src, whole(h), sumsq_dev))) return rc;
   h->spill_valid = h->d.gbar_ws != nullptr;
   return ZS_OK;
 }
@@ -1233,7 +1263,8 @@ int run_gnorm_bucketed(zs_handle *h, const Src &src, int64_t bucket_len, int32_t
     const int64_t off = j * bucket_len;
     const Part part{off, n - off < bucket_len ? n - off : bucket_len, h->workers[w],
                     h->bucket_partials + int64_t(w) * h->bucket_part_len};
-    if ((rc = launch_gnorm(h, src, part, h->bucket_sums + j))) return rc;
+    if ((rc = launch_gnorm(h->d.n_d, h->d.gbar_ws, src, part, h->bucket_sums + j)))
+      return rc;
   }
   if ((rc = join_workers(h, streams))) return rc;
   hipLaunchKernelGGL(bucket_sum_kernel, dim3(1), dim3(64), 0,
@@ -1280,6 +1311,7 @@ const char *zero_shard_strerror(int code) {
     case ZS_EHIP: return "HIP runtime error or kernel launch failure";
     case ZS_EDEVICE: return "current device is not the gfx950 the handle was made on";
     case ZS_ESTATE: return "call out of order or handle not live";
+    case ZS_ETOOBIG: return "shard too long for the allocation-free call's static scratch";
     default: return "unknown zero_shard status";
   }
 }
@@ -1309,6 +1341,10 @@ int zero_shard_init(const zs_desc *d, zs_handle **out) {
   hipDeviceProp_t prop;
   if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return ZS_EHIP;
   if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) return ZS_EDEVICE;
+  // the allocation-free calls' scratch on this device: resolved here, at
+  // set-up, so that those calls never have to
+  double *static_partials = nullptr;
+  if (int rc = scratch_address(&static_partials)) return rc;
   zs_handle *h = new (std::nothrow) zs_handle();
   if (!h) return ZS_ENOMEM;
   h->magic = kMagic;
@@ -1333,7 +1369,7 @@ int zero_shard_gnorm(zs_handle *h, const zs_bf16 *const *contrib, double *sumsq_
   std::memset(&src, 0, sizeof src);
   int rc = gnorm_args_ok(h, sumsq_dev);
   if (rc) return rc;
-  if (h->d.shard_len > 0 && (rc = check_rows(h, contrib, &src))) return rc;
+  if (h->d.shard_len > 0 && (rc = check_rows(h->d.n_d, contrib, &src))) return rc;
   return run_gnorm(h, src, sumsq_dev);
 }
 
@@ -1348,6 +1384,27 @@ int zero_shard_gnorm_q8(zs_handle *h, const int8_t *const *codes, const float *c
   return run_gnorm(h, src, sumsq_dev);
 }
 
+int zero_shard_gnorm_noalloc(const zs_desc *d, const zs_bf16 *const *contrib,
+                             double *sumsq_dev) {
+  if (!d || !sumsq_dev) return ZS_EINVAL;
+  if (!zs_args::geometry_ok(*d)) return ZS_EINVAL;
+  if (!aligned(sumsq_dev, 8)) return ZS_EALIGN;
+  const int64_t n = d->shard_len;
+  Bf16Rows src;
+  std::memset(&src, 0, sizeof src);
+  if (n > 0) {
+    if (d->gbar_ws && !aligned(d->gbar_ws, 16)) return ZS_EALIGN;
+    if (int rc = check_rows(d->n_d, contrib, &src)) return rc;
+  }
+  if (norm_blocks<Bf16Rows>(n) > kStaticPartials) return ZS_ETOOBIG;
+  int rc = device_is_gfx950();
+  if (rc) return rc;
+  double *partials = nullptr;
+  if ((rc = scratch_address(&partials))) return rc;
+  const Part part{0, n, static_cast<hipStream_t>(d->stream), partials};
+  return launch_gnorm(d->n_d, d->gbar_ws, src, part, sumsq_dev);
+}
+
 int zero_shard_step(zs_handle *h, const zs_bf16 *const *contrib, float lr, int64_t t,
                     const double *global_sumsq_dev) {
   Bf16Rows src;
@@ -1355,7 +1412,7 @@ int zero_shard_step(zs_handle *h, const zs_bf16 *const *contrib, float lr, int64
   bool spill = false;
   int rc = step_args_ok(h, lr, t, global_sumsq_dev, &spill);
   if (rc) return rc;
-  if (h->d.shard_len > 0 && !spill && (rc = check_rows(h, contrib, &src))) return rc;
+  if (h->d.shard_len > 0 && !spill && (rc = check_rows(h->d.n_d, contrib, &src))) return rc;
   return run_step(h, src, lr, t, global_sumsq_dev, spill);
 }
 
@@ -1442,7 +1499,7 @@ int zero_shard_gnorm_bucketed(zs_handle *h, const zs_bf16 *const *contrib, int64
   int rc = gnorm_args_ok(h, sumsq_dev);
   if (rc) return rc;
   if ((rc = bucket_args_ok(h, bucket_len, streams))) return rc;
-  if (h->d.shard_len > 0 && (rc = check_rows(h, contrib, &src))) return rc;
+  if (h->d.shard_len > 0 && (rc = check_rows(h->d.n_d, contrib, &src))) return rc;
   return run_gnorm_bucketed(h, src, bucket_len, streams, ready, sumsq_dev);
 }
 
@@ -1468,7 +1525,7 @@ int zero_shard_step_bucketed(zs_handle *h, const zs_bf16 *const *contrib, int64_
   int rc = step_args_ok(h, lr, t, global_sumsq_dev, &use_spill);
   if (rc) return rc;
   if ((rc = bucket_args_ok(h, bucket_len, streams))) return rc;
-  if (h->d.shard_len > 0 && !use_spill && (rc = check_rows(h, contrib, &src))) return rc;
+  if (h->d.shard_len > 0 && !use_spill && (rc = check_rows(h->d.n_d, contrib, &src))) return rc;
   return run_step_bucketed(h, src, bucket_len, streams, ready, lr, t, global_sumsq_dev,
                            use_spill);
 }

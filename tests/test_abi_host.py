@@ -70,7 +70,7 @@ def test_partition_geometry():
 
 
 def test_strerror():
-    for c in (0, -1, -2, -3, -4, -5, -6):
+    for c in (0, -1, -2, -3, -4, -5, -6, -7):
         assert Z.zero_shard_strerror(c)
     assert "unknown" in Z.zero_shard_strerror(-99)
 
@@ -201,3 +201,27 @@ def test_offload_init_rejects_bad_hyperparameters_before_allocating():
                 dict(phi=n, n_d=2, r=2), dict(phi=n, n_d=2, r=1, shard_len=n)):
         rc, o = init(**bad)
         assert rc == Z.ZS_EINVAL and not o.value, bad
+
+
+def test_noalloc_norm_rejects_bad_arguments_before_the_device():
+    """zero_shard_gnorm_noalloc validates its descriptor, pointers and size
+    before it touches a device (pointers here are never dereferenced)."""
+    rows = (ctypes.c_void_p * 4)(*[0x100000 + 0x1000 * k for k in range(4)])
+    s = ctypes.c_void_p(0x200000)
+    lib = Z._lib
+
+    def call(desc, contrib=rows, sumsq=s):
+        return lib.zero_shard_gnorm_noalloc(ctypes.byref(desc) if desc is not None else None,
+                                            contrib, sumsq)
+
+    assert call(None) == Z.ZS_EINVAL
+    assert call(_desc(), sumsq=None) == Z.ZS_EINVAL
+    assert call(_desc(r=4)) == Z.ZS_EINVAL
+    assert call(_desc(shard_len=1000)) == Z.ZS_EINVAL
+    assert call(_desc(), sumsq=ctypes.c_void_p(0x200004)) == Z.ZS_EALIGN
+    assert call(_desc(gbar_ws=0x70004)) == Z.ZS_EALIGN
+    assert call(_desc(), contrib=None) == Z.ZS_EINVAL
+    bad = (ctypes.c_void_p * 4)(0x100000, 0x100008, 0x102000, 0x103000)
+    assert call(_desc(), contrib=bad) == Z.ZS_EALIGN
+    big = (1 << 30) + 8
+    assert call(_desc(phi=big, n_d=4, r=0, shard_len=big)) == Z.ZS_ETOOBIG
