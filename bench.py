@@ -433,6 +433,111 @@ def bench_overlap(w, args) -> int:
     return 0
 
 
+def bench_graph(w, args) -> int:
+    """Launch-bound workloads (the tiny shard is cache-resident: its kernel
+    takes a few microseconds): the same steps timed (a) eagerly, one
+    zero_shard_step call per step, (b) as one captured step replayed per
+    step, its constants (lr, lr*wd, bias corrections) copied to the device
+    before each replay, (c) as one graph of K steps reading K rows of a
+    constants table, replayed once.  HIP events on the handle's stream; the
+    results of (b) and (c) are checked against (a) bit for bit."""
+    import numpy as np
+    import torch
+
+    from tests._gpu import GpuShard
+
+    K = args.steps
+    side = torch.cuda.Stream()
+    n = w.shard_len
+    _eprint(f"[bench] graph {w.name}: shard {n}, {K} steps")
+    gs = {k: GpuShard(w, stream=side) for k in ("eager", "graph1", "graphK")}
+    for g in gs.values():
+        g.init_state()
+        g.fill_grads(1)
+    torch.cuda.synchronize()
+    spill = w.max_norm > 0
+
+    def step_dev(g, cdev):
+        if g.clip:
+            g.norm()
+        g.shard.step_dev(None if spill else g.tab, cdev, g.sumsq if g.clip else None)
+
+    consts = torch.zeros(4, dtype=torch.float64, device="cuda")
+    table = torch.zeros(K, 4, dtype=torch.float64, device="cuda")
+    g1, gK = gs["graph1"], gs["graphK"]
+    graph1, graphK = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph1, stream=side):
+        step_dev(g1, consts)
+    with torch.cuda.graph(graphK, stream=side):
+        for j in range(K):
+            step_dev(gK, table[j])
+    torch.cuda.synchronize()
+    cst = {s: g1.shard.consts(w.lr, w.t_of(s)) for s in range(1, 2 * K + 1)}
+    # every step's constants in pinned memory up front: no host buffer is
+    # rewritten while an asynchronous copy from it may be pending
+    pinned = torch.tensor([[0.0] * 4] + [cst[s] for s in range(1, 2 * K + 1)],
+                          dtype=torch.float64).pin_memory()
+
+    def timed(fn):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        a.record(side)
+        fn()
+        b.record(side)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / K, (time.perf_counter() - t0) * 1e6 / K
+
+    def run_eager(s0):
+        with torch.cuda.stream(side):
+            for s in range(s0, s0 + K):
+                gs["eager"].step(s)
+
+    def run_graph1(s0):
+        with torch.cuda.stream(side):
+            for s in range(s0, s0 + K):
+                consts.copy_(pinned[s], non_blocking=True)
+                graph1.replay()
+
+    def run_graphK(s0):
+        with torch.cuda.stream(side):
+            table.copy_(pinned[s0:s0 + K], non_blocking=True)
+            graphK.replay()
+
+    res = {}
+    for name, fn in (("eager", run_eager), ("graph1", run_graph1), ("graphK", run_graphK)):
+        fn(1)  # warm-up: steps 1..K
+        res[name] = timed(lambda: fn(K + 1))  # steps K+1..2K
+        _eprint(f"[bench] {name}: {res[name][0]:.2f} us per step (events), "
+                f"{res[name][1]:.2f} us per step (wall clock)")
+    ref = gs["eager"].host()
+    for name in ("graph1", "graphK"):
+        got = gs[name].host()
+        for k in ref:
+            assert np.array_equal(ref[k].view(np.uint8), got[k].view(np.uint8)), (name, k)
+    _eprint("[bench] graph replays equal the eager steps bit for bit")
+    for g in gs.values():
+        g.free()
+    us = res["graphK"][1]
+    kb = sum(kernel_bytes(w, spill).values())
+    line = {
+        "metric": METRIC + " (launch-bound workload: eager vs captured steps)",
+        "value": n / (us * 1e-6), "unit": "params/s", "n_gpus": 1, "steps": K,
+        "warmup": K, "ms_per_step": us / 1e3, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f64", "data": "synthetic",
+        "config": {"workload": f"{w.name} graph of {K} steps", "phi": w.phi, "n_d": w.n_d,
+                   "shard_len": n},
+        "graph": {k: {"us_per_step_events": round(v[0], 3), "us_per_step_wall": round(v[1], 3)}
+                  for k, v in res.items()},
+        "hbm": {"bytes_per_param": kb,
+                "GBps_graphK": round(kb * n / (res["graphK"][0] * 1e-6) / 1e9, 1),
+                "note": "cache-resident (the shard's state fits the last-level cache)"},
+        "roofline": None, "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -461,6 +566,9 @@ def main() -> int:
                     help="with --bucket: buckets arrive over a link of GBPS GB/s (a timed wait "
                          "per bucket on another stream), and the bucketed step overlaps the "
                          "arrivals; compared with waiting for all buckets")
+    ap.add_argument("--graph", action="store_true",
+                    help="launch-bound workloads: eager steps against one captured step "
+                         "replayed per step and against a graph of --steps steps")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run torch copies of MIB MiB (for HBM counter scaling)")
     args = ap.parse_args()
@@ -494,6 +602,8 @@ def main() -> int:
         return bench_dequant(w, args)
     if args.offload:
         return bench_offload(w, args)
+    if args.graph:
+        return bench_graph(w, args)
     if args.arrive_gbps:
         if not args.bucket:
             _eprint("[bench] --arrive-gbps needs --bucket")

@@ -160,10 +160,31 @@ int zero_shard_gnorm_noalloc(const zs_desc *d, const zs_bf16 *const *contrib,
  * host synchronisation is needed between gnorm and step.  gnorm and step
  * queue kernel launches only (no allocation, no memset), so they can be
  * captured in a HIP graph on the handle's stream; t and lr are then fixed
- * in the captured launches.
+ * in the captured launches (zero_shard_step_dev reads them from device
+ * memory instead).
  * Errors: ZS_EINVAL, ZS_EALIGN, ZS_ESTATE, ZS_EHIP. */
 int zero_shard_step(zs_handle *h, const zs_bf16 *const *contrib, float lr, int64_t t,
                     const double *global_sumsq_dev);
+
+/* The constants of step t at learning rate lr as the library computes them
+ * on the host for zero_shard_step: out[0] = lr, out[1] = lr * weight_decay,
+ * out[2] = bc1 = 1 - beta1^t, out[3] = bc2 = 1 - beta2^t (1 and 1 without
+ * bias correction), binary64 from d's binary32 values (pow of the C
+ * library).  out is a HOST array of 4 doubles; only d's hyper-parameters are
+ * read.  Errors: ZS_EINVAL (bad d, lr or t). */
+int zero_shard_step_consts(const zs_desc *d, float lr, int64_t t, double *out);
+
+/* zero_shard_step with the step's constants read on the device, when the
+ * kernel runs, from consts_dev (device, 4 doubles, 8-byte aligned, laid out
+ * as zero_shard_step_consts writes them) instead of fixed at the call.  A
+ * step captured in a HIP graph then serves every step: before each replay
+ * the caller writes that step's constants to consts_dev (outside the graph,
+ * e.g. an asynchronous copy on the same stream).  With the constants of
+ * (lr, t) the results are zero_shard_step's at (lr, t), bit for bit.  The
+ * constants are trusted as given.  Errors: ZS_EINVAL, ZS_EALIGN, ZS_ESTATE,
+ * ZS_EHIP. */
+int zero_shard_step_dev(zs_handle *h, const zs_bf16 *const *contrib, const double *consts_dev,
+                        const double *global_sumsq_dev);
 
 /* a1 with int8 contributions: ZeRO++ qgZ ("ZeRO (딥 러닝)", follow-ups table
  * "후속 기법": gradients are quantized and averaged after an all-to-all).

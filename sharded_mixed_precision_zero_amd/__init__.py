@@ -63,6 +63,11 @@ _lib.zero_shard_init.restype = ctypes.c_int
 _lib.zero_shard_init.argtypes = [ctypes.POINTER(zs_desc), ctypes.POINTER(_handle_p)]
 _lib.zero_shard_gnorm.restype = ctypes.c_int
 _lib.zero_shard_gnorm.argtypes = [_handle_p, ctypes.c_void_p, ctypes.c_void_p]
+_lib.zero_shard_step_consts.restype = ctypes.c_int
+_lib.zero_shard_step_consts.argtypes = [ctypes.POINTER(zs_desc), ctypes.c_float, ctypes.c_int64,
+                                        ctypes.c_void_p]
+_lib.zero_shard_step_dev.restype = ctypes.c_int
+_lib.zero_shard_step_dev.argtypes = [_handle_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
 _lib.zero_shard_gnorm_noalloc.restype = ctypes.c_int
 _lib.zero_shard_gnorm_noalloc.argtypes = [ctypes.POINTER(zs_desc), ctypes.c_void_p,
                                           ctypes.c_void_p]
@@ -121,6 +126,7 @@ _lib.zero_shard_len.restype = ctypes.c_int64
 _lib.zero_shard_len.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32]
 
 EXPORTS = ("zero_shard_init", "zero_shard_gnorm", "zero_shard_gnorm_noalloc", "zero_shard_step",
+           "zero_shard_step_consts", "zero_shard_step_dev",
            "zero_shard_gnorm_q8",
            "zero_shard_step_q8", "zero_shard_gnorm_bucketed", "zero_shard_step_bucketed",
            "zero_shard_gnorm_bucketed_q8", "zero_shard_step_bucketed_q8",
@@ -193,6 +199,19 @@ def zero_shard_gnorm_noalloc(desc: zs_desc, contrib, sumsq_dev) -> int:
 def zero_shard_step(h, contrib, lr: float, t: int, global_sumsq_dev=None) -> int:
     return _lib.zero_shard_step(h, contrib_table(contrib), float(lr), int(t),
                                 _ptr(global_sumsq_dev))
+
+
+def zero_shard_step_consts(desc: zs_desc, lr: float, t: int):
+    """-> (status, [lr, lr*wd, bc1, bc2]) as the library computes them."""
+    out = (ctypes.c_double * 4)()
+    rc = _lib.zero_shard_step_consts(ctypes.byref(desc), float(lr), int(t), out)
+    return rc, list(out)
+
+
+def zero_shard_step_dev(h, contrib, consts_dev, global_sumsq_dev=None) -> int:
+    """consts_dev: a float64 device tensor of 4 (see zero_shard_step_consts)."""
+    return _lib.zero_shard_step_dev(h, contrib_table(contrib), _ptr(consts_dev),
+                                    _ptr(global_sumsq_dev))
 
 
 def zero_shard_gnorm_q8(h, codes, scales, block: int, sumsq_dev) -> int:
@@ -360,6 +379,15 @@ class ZeroShard:
 
     def step(self, contrib, lr: float, t: int, global_sumsq_dev=None) -> None:
         _check(zero_shard_step(self.h, contrib, lr, t, global_sumsq_dev), "zero_shard_step")
+
+    def step_dev(self, contrib, consts_dev, global_sumsq_dev=None) -> None:
+        _check(zero_shard_step_dev(self.h, contrib, consts_dev, global_sumsq_dev),
+               "zero_shard_step_dev")
+
+    def consts(self, lr: float, t: int) -> list[float]:
+        rc, out = zero_shard_step_consts(self.desc, lr, t)
+        _check(rc, "zero_shard_step_consts")
+        return out
 
     def gnorm_q8(self, codes, scales, block: int, sumsq_dev) -> None:
         _check(zero_shard_gnorm_q8(self.h, codes, scales, block, sumsq_dev), "zero_shard_gnorm_q8")

@@ -138,6 +138,7 @@ struct StepArgs {
   Src src;
   Avg avg;
   AdamConst k;
+  const double *dyn;    // iff non-null: lr, lr*wd, bc1, bc2 read from here at run time
   int64_t n;
   const double *sumsq;  // clip by this global sum of squares iff non-null
   double max_norm;
@@ -404,7 +405,8 @@ __device__ __forceinline__ void reduce_average_wave(const Src &src, const Avg &a
 // valid elements.  Every lane of the wave calls it together (the quantizer
 // reduces across lanes); lanes past the end pass a vector with nvalid 0.
 template <int QL, class Src>
-__device__ __forceinline__ void step_vec(const StepArgs<Src> &A, int64_t vec, double coef) {
+__device__ __forceinline__ void step_vec(const StepArgs<Src> &A, const AdamConst &k, int64_t vec,
+                                         double coef) {
     const int64_t e0 = vec * kVec;
     const int nvalid = e0 + kVec <= A.n ? kVec : (e0 < A.n ? int(A.n - e0) : 0);
     float th[kVec], mo[kVec], va[kVec], g[kVec], p[kVec];
@@ -446,7 +448,7 @@ __device__ __forceinline__ void step_vec(const StepArgs<Src> &A, int64_t vec, do
       }
 #pragma unroll
       for (int e = 0; e < kVec; ++e) {
-        adam(coef * static_cast<double>(g[e]), th[e], mo[e], va[e], A.k);
+        adam(coef * static_cast<double>(g[e]), th[e], mo[e], va[e], k);
       }
     }
     unsigned pb[4];
@@ -508,8 +510,9 @@ __device__ __forceinline__ void load_state(const StepArgs<Src> &A, int64_t vec, 
 // gradient is g and whose state was loaded into s; every lane of the wave
 // calls it together when QL > 0.
 template <int QL, class Src>
-__device__ __forceinline__ void update_full(const StepArgs<Src> &A, int64_t vec, double coef,
-                                            const float (&g)[kVec], const StateFrag &s) {
+__device__ __forceinline__ void update_full(const StepArgs<Src> &A, const AdamConst &k,
+                                            int64_t vec, double coef, const float (&g)[kVec],
+                                            const StateFrag &s) {
   constexpr bool nt = ZS_NT_STATE;
   float th[kVec], mo[kVec], va[kVec], p[kVec];
 #pragma unroll
@@ -519,7 +522,7 @@ __device__ __forceinline__ void update_full(const StepArgs<Src> &A, int64_t vec,
     va[e] = s.v[0][e]; va[e + 4] = s.v[1][e];
   }
 #pragma unroll
-  for (int e = 0; e < kVec; ++e) adam(coef * static_cast<double>(g[e]), th[e], mo[e], va[e], A.k);
+  for (int e = 0; e < kVec; ++e) adam(coef * static_cast<double>(g[e]), th[e], mo[e], va[e], k);
   unsigned pb[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
@@ -546,6 +549,20 @@ __device__ __forceinline__ void update_full(const StepArgs<Src> &A, int64_t vec,
   if constexpr (QL > 0) quant_lane<QL>(p, kVec, vec, A.codes, A.scales);
 }
 
+// The step's constants: fixed at the call, or read from the caller's device
+// array when the launch carries one (a graph replayed at every step).
+template <class Src>
+__device__ __forceinline__ AdamConst step_consts(const StepArgs<Src> &A) {
+  AdamConst k = A.k;
+  if (A.dyn) {
+    k.lr = A.dyn[0];
+    k.decay = A.dyn[1];
+    k.bc1 = A.dyn[2];
+    k.bc2 = A.dyn[3];
+  }
+  return k;
+}
+
 #ifndef ZS_WIDE_MIN_ROWS
 #define ZS_WIDE_MIN_ROWS 16
 #endif
@@ -568,12 +585,13 @@ __global__ void __launch_bounds__(kThreads) step_kernel(const StepArgs<Src> A) {
   const int64_t nfull = A.n / kVec;
   const int64_t stride = int64_t(gridDim.x) * (kThreads / 64) * span;
   const double coef = A.sumsq ? clip_coef(*A.sumsq, A.max_norm) : 1.0;
+  const AdamConst k = step_consts(A);
   constexpr bool nt = ZS_NT_STATE;
   for (int64_t wb = (int64_t(blockIdx.x) * (kThreads / 64) + wave) * span; wb < nvec;
        wb += stride) {
     if (U == 1 || wb + span > nfull) {
 #pragma unroll
-      for (int u = 0; u < U; ++u) step_vec<QL, Src>(A, wb + 64 * u + lane, coef);
+      for (int u = 0; u < U; ++u) step_vec<QL, Src>(A, k, wb + 64 * u + lane, coef);
       continue;
     }
     float g[U][kVec];
@@ -583,7 +601,7 @@ __global__ void __launch_bounds__(kThreads) step_kernel(const StepArgs<Src> A) {
       const int64_t vec = wb + 64 * u + lane;
       StateFrag sf;
       load_state<nt>(A, vec, sf);
-      update_full<QL>(A, vec, coef, g[u], sf);
+      update_full<QL>(A, k, vec, coef, g[u], sf);
     }
   }
 }
@@ -1058,6 +1076,17 @@ int run_gnorm(zs_handle *h, const Src &src, double *sumsq_dev) {
 }
 
 int step_args_ok(zs_handle *h, float lr, int64_t t, const double *global_sumsq_dev,
+                 bool *use_spill);
+
+// The checks of a step whose constants the device reads from consts_dev.
+int step_dev_args_ok(zs_handle *h, const double *consts_dev, const double *global_sumsq_dev,
+                     bool *use_spill) {
+  if (!consts_dev) return live(h) ? ZS_EINVAL : ZS_ESTATE;
+  if (!aligned(consts_dev, 8)) return live(h) ? ZS_EALIGN : ZS_ESTATE;
+  return step_args_ok(h, 0.0f, 1, global_sumsq_dev, use_spill);
+}
+
+int step_args_ok(zs_handle *h, float lr, int64_t t, const double *global_sumsq_dev,
                  bool *use_spill) {
   if (!live(h)) return ZS_ESTATE;
   const zs_desc &d = h->d;
@@ -1073,8 +1102,33 @@ int step_args_ok(zs_handle *h, float lr, int64_t t, const double *global_sumsq_d
 
 // a1 + a2 (apply) + a3 + a4 (+ a5) over one part, after the arguments
 // were checked.
+// The update's constants at step t with learning rate lr, binary64 from the
+// descriptor's binary32 values (the device reads lr, lr*wd, bc1 and bc2
+// from a caller's array instead when a launch carries one).
+AdamConst make_consts(const zs_desc &d, float lr, int64_t t) {
+  AdamConst k;
+  const double b1 = d.beta1, b2 = d.beta2;
+  k.b1 = b1;
+  k.omb1 = 1.0 - b1;
+  k.b2 = b2;
+  k.omb2 = 1.0 - b2;
+  k.bc1 = d.bias_correction ? 1.0 - std::pow(b1, double(t)) : 1.0;
+  k.bc2 = d.bias_correction ? 1.0 - std::pow(b2, double(t)) : 1.0;
+  k.lr = double(lr);
+  k.decay = double(lr) * double(d.weight_decay);
+  k.eps = double(d.eps);
+  return k;
+}
+
+// The step's constants as a launch takes them: fixed (k), or read on the
+// device from dyn when dyn is non-null.
+struct StepTime {
+  AdamConst k;
+  const double *dyn;
+};
+
 template <class Src>
-int launch_step(zs_handle *h, const Src &src, const Part &part, float lr, int64_t t,
+int launch_step(zs_handle *h, const Src &src, const Part &part, const StepTime &when,
                 const double *global_sumsq_dev, bool use_spill) {
   const zs_desc &d = h->d;
   const int64_t n = part.len, off = part.off;
@@ -1083,16 +1137,8 @@ int launch_step(zs_handle *h, const Src &src, const Part &part, float lr, int64_
   StepArgs<Src> A;
   A.src = use_spill ? src : shifted(src, d.n_d, off);
   A.avg = make_avg(d.n_d);
-  const double b1 = d.beta1, b2 = d.beta2;
-  A.k.b1 = b1;
-  A.k.omb1 = 1.0 - b1;
-  A.k.b2 = b2;
-  A.k.omb2 = 1.0 - b2;
-  A.k.bc1 = d.bias_correction ? 1.0 - std::pow(b1, double(t)) : 1.0;
-  A.k.bc2 = d.bias_correction ? 1.0 - std::pow(b2, double(t)) : 1.0;
-  A.k.lr = double(lr);
-  A.k.decay = double(lr) * double(d.weight_decay);
-  A.k.eps = double(d.eps);
+  A.k = when.k;
+  A.dyn = when.dyn;
   A.n = n;
   A.sumsq = clip ? global_sumsq_dev : nullptr;
   A.max_norm = double(d.max_norm);
@@ -1129,12 +1175,12 @@ int launch_step(zs_handle *h, const Src &src, const Part &part, float lr, int64_
 }
 
 template <class Src>
-int run_step(zs_handle *h, const Src &src, float lr, int64_t t, const double *global_sumsq_dev,
+int run_step(zs_handle *h, const Src &src, const StepTime &when, const double *global_sumsq_dev,
              bool use_spill) {
   int rc = current_device_ok(h);
   if (rc) return rc;
   h->spill_valid = false;
-  return launch_step(h, src, whole(h), lr, t, global_sumsq_dev, use_spill);
+  return launch_step(h, src, whole(h), when, global_sumsq_dev, use_spill);
 }
 
 // ------------------------------------------------------------ bucketed calls
@@ -1293,7 +1339,9 @@ int run_step_bucketed(zs_handle *h, const Src &src, int64_t bucket_len, int32_t 
     if ((rc = wait_ready(h->workers[w], ready, j))) return rc;
     const int64_t off = j * bucket_len;
     const Part part{off, n - off < bucket_len ? n - off : bucket_len, h->workers[w], nullptr};
-    if ((rc = launch_step(h, src, part, lr, t, global_sumsq_dev, use_spill))) return rc;
+    if ((rc = launch_step(h, src, part, StepTime{make_consts(h->d, lr, t), nullptr},
+                          global_sumsq_dev, use_spill)))
+      return rc;
   }
   return join_workers(h, streams);
 }
@@ -1413,7 +1461,31 @@ int zero_shard_step(zs_handle *h, const zs_bf16 *const *contrib, float lr, int64
   int rc = step_args_ok(h, lr, t, global_sumsq_dev, &spill);
   if (rc) return rc;
   if (h->d.shard_len > 0 && !spill && (rc = check_rows(h->d.n_d, contrib, &src))) return rc;
-  return run_step(h, src, lr, t, global_sumsq_dev, spill);
+  return run_step(h, src, StepTime{make_consts(h->d, lr, t), nullptr}, global_sumsq_dev, spill);
+}
+
+int zero_shard_step_consts(const zs_desc *d, float lr, int64_t t, double *out) {
+  if (!d || !out) return ZS_EINVAL;
+  if (!zs_args::hyper_ok(*d) || !zs_args::step_ok(lr, t)) return ZS_EINVAL;
+  const AdamConst k = make_consts(*d, lr, t);
+  out[0] = k.lr;
+  out[1] = k.decay;
+  out[2] = k.bc1;
+  out[3] = k.bc2;
+  return ZS_OK;
+}
+
+int zero_shard_step_dev(zs_handle *h, const zs_bf16 *const *contrib, const double *consts_dev,
+                        const double *global_sumsq_dev) {
+  Bf16Rows src;
+  std::memset(&src, 0, sizeof src);
+  bool spill = false;
+  int rc = step_dev_args_ok(h, consts_dev, global_sumsq_dev, &spill);
+  if (rc) return rc;
+  if (h->d.shard_len > 0 && !spill && (rc = check_rows(h->d.n_d, contrib, &src))) return rc;
+  // b1, b2, eps from the descriptor; lr, lr*wd, bc1, bc2 from consts_dev
+  return run_step(h, src, StepTime{make_consts(h->d, 0.0f, 1), consts_dev}, global_sumsq_dev,
+                  spill);
 }
 
 int zero_shard_step_q8(zs_handle *h, const int8_t *const *codes, const float *const *scales,
@@ -1425,7 +1497,7 @@ int zero_shard_step_q8(zs_handle *h, const int8_t *const *codes, const float *co
   if (rc) return rc;
   if (!spill && quant_lanes(block) < 0) return ZS_EINVAL;
   if (h->d.shard_len > 0 && !spill && (rc = check_q8(h, codes, scales, block, &src))) return rc;
-  return run_step(h, src, lr, t, global_sumsq_dev, spill);
+  return run_step(h, src, StepTime{make_consts(h->d, lr, t), nullptr}, global_sumsq_dev, spill);
 }
 
 int zero_shard_quant(zs_handle *h, int32_t block) {

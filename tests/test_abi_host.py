@@ -225,3 +225,25 @@ def test_noalloc_norm_rejects_bad_arguments_before_the_device():
     assert call(_desc(), contrib=bad) == Z.ZS_EALIGN
     big = (1 << 30) + 8
     assert call(_desc(phi=big, n_d=4, r=0, shard_len=big)) == Z.ZS_ETOOBIG
+
+
+def test_step_constants():
+    """zero_shard_step_consts: lr, lr * wd, 1 - beta1^t, 1 - beta2^t in
+    binary64 from the binary32 hyper-parameters (1, 1 without bias
+    correction); bad arguments are refused."""
+    import math
+
+    import numpy as np
+
+    f = lambda x: float(np.float32(x))  # noqa: E731
+    for t in (1, 2, 7, 1000, 1050):
+        d = _desc(beta1=0.9, beta2=0.95, weight_decay=0.1)
+        rc, out = Z.zero_shard_step_consts(d, 1e-4, t)
+        assert rc == Z.ZS_OK
+        assert out == [f(1e-4), f(1e-4) * f(0.1), 1.0 - math.pow(f(0.9), t),
+                       1.0 - math.pow(f(0.95), t)]
+    rc, out = Z.zero_shard_step_consts(_desc(bias_correction=0), 1e-3, 5)
+    assert rc == Z.ZS_OK and out[2:] == [1.0, 1.0]
+    for bad in ((_desc(), -1.0, 1), (_desc(), float("inf"), 1), (_desc(), 1e-3, 0),
+                (_desc(beta1=1.0), 1e-3, 1)):
+        assert Z.zero_shard_step_consts(*bad)[0] == Z.ZS_EINVAL
