@@ -1,47 +1,73 @@
-// hbm_probe.hip -- HBM bandwidth ceiling of MI355X for read/write mixes.
+// hbm_probe.hip -- what the MI355X memory system sustains for the read/write
+// mixes of the shard-step kernels, over a sweep of access shapes.
 //
-// Measures streaming kernels with R read streams and W write streams of
-// 16-byte vectors (each wave sweeps U consecutive 1 KiB runs of every
-// stream per iteration, as the shard-step kernels do), so that a kernel's
-// achieved GB/s can be set against what the memory system sustains for the
-// same mix on the same box.  Two launch shapes: a fixed grid striding over
-// the streams, and a one-shot grid (one sweep per wave) laid out as F
-// separated fronts, as the norm pass is.  Stream i starts i * 1280 bytes
-// past a 2 MiB boundary, so that the streams do not all hit the same HBM
-// channel at the same offset (the shard-step rows are staggered the same
-// way).  Mixes, per 8 shard elements:
-//   R1W0   pure read                    R0W1   pure write
-//   R1W1   copy
-//   R16W2  norm pass at N_d = 16: 16 bf16 rows in, fp32 spill out
-//   R8W8   clipped update: spill + fp32 state in, state + bf16 + int8 out
-//   R64W0  the rows of the N_d = 64 update (plus its small state stream)
-// Every access is in bounds: the sweep stops at the last whole chunk.
-// Build and run:  hipcc --offload-arch=gfx950 -O3 hbm_probe.hip -o hbm_probe
+// A probe kernel streams R read streams and W write streams of 16-byte
+// vectors: each wave sweeps U consecutive 1 KiB runs of every stream (lane l
+// takes vectors v0+l, v0+64+l, ...), sums what it read and writes that sum
+// (+ the stream index) to every write stream, so writes follow their reads
+// as in the shard step.  The sweep varies, per mix:
+//   * load policy: plain or nontemporal;  store policy: plain or nontemporal;
+//   * U (lane-vectors per wave sweep): 1, 2, 4, 8;
+//   * grid: one-shot (one sweep per wave), optionally with the blocks
+//     regrouped so that each XCD (blocks are dealt to the 8 XCDs round-robin)
+//     streams one contiguous stretch; or persistent (k workgroups per CU,
+//     grid-stride loop);
+//   * workgroups resident per CU: as many as fit, or capped at 1, 2, 3 or 4
+//     by a dynamic LDS reservation (with and without the XCD regrouping);
+//   * stream layout: consecutive streams 1280 B apart past a 2 MiB boundary,
+//     exactly 2 MiB-aligned, or 64 KiB + 1280 B apart.
+// Mixes (16-byte vectors per 8 shard elements), named for the kernel whose
+// traffic they reproduce:
+//   read   R1  W0   pure read           write  R0 W1  pure write
+//   copy   R1  W1
+//   norm16 R16 W2   norm pass, N_d = 16: 16 bf16 rows in, fp32 spill out
+//   upd    R8  W7   clipped update: spill + fp32 state in, state + bf16 out
+//   nd1    R7  W7   N_d = 1 update: one bf16 row + state in, state + bf16 out
+//   nd64   R70 W7   N_d = 64 update: 64 bf16 rows + state in, state + bf16 out
+//   q8nd64 R38 W7   N_d = 64 int8 rows (8 B per lane-vector) + state in
+// Every access is in bounds: a stream holds n vectors, n a multiple of every
+// sweep span times 8, one-shot grids cover exactly n, persistent loops stop
+// at the last whole span.  Prints one line per configuration and the best
+// per mix.
+// Build:  hipcc --offload-arch=gfx950 -O3 hbm_probe.hip -o hbm_probe
+// Run:    hbm_probe [mix ...]   (default: every mix)
 #include <hip/hip_runtime.h>
 
 #include <cstdio>
 #include <cstdlib>
+#include <cstring>
+#include <string>
+#include <vector>
 
 using u32x4 = unsigned int __attribute__((ext_vector_type(4)));
-constexpr int kMaxIn = 64, kMaxOut = 8;
+constexpr int kMaxIn = 70, kMaxOut = 7;
 struct Streams {
   const u32x4 *in[kMaxIn];
   u32x4 *out[kMaxOut];
 };
 
-// F = 0: fixed grid, grid-stride loop.  F > 0: one sweep per wave, block b
-// in front b mod F (the grid is a multiple of F).
-template <int R, int W, int U, int F>
-__global__ void __launch_bounds__(256) probe(const Streams S, long n, unsigned *sink) {
+template <bool NT>
+__device__ __forceinline__ u32x4 load(const u32x4 *p) {
+  if constexpr (NT) return __builtin_nontemporal_load(p);
+  else return *p;
+}
+template <bool NT>
+__device__ __forceinline__ void store(u32x4 v, u32x4 *p) {
+  if constexpr (NT) __builtin_nontemporal_store(v, p);
+  else *p = v;
+}
+
+// mode 0: one-shot, block b at its own index; mode 1: one-shot, blocks
+// regrouped per XCD (grid a multiple of 8); mode 2: persistent grid-stride.
+template <int R, int W, int U, bool LNT, bool SNT>
+__global__ void __launch_bounds__(256) probe(const Streams S, long n, int mode, unsigned *sink) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const long span = 64L * U;
-  long first = ((long)blockIdx.x * 4 + wave) * span, stride = (long)gridDim.x * 4 * span;
-  if (F > 0) {
-    const long per_front = (long)gridDim.x / (F > 0 ? F : 1);
-    const long slot = (long)(blockIdx.x % (F > 0 ? F : 1)) * per_front + blockIdx.x / (F > 0 ? F : 1);
-    first = (slot * 4 + wave) * span;
-    stride = n;  // one sweep
-  }
+  const long grid = gridDim.x;
+  long blk = blockIdx.x;
+  if (mode == 1) blk = (blk % 8) * (grid / 8) + blk / 8;
+  const long first = (blk * 4 + wave) * span;
+  const long stride = mode == 2 ? grid * 4 * span : n;
   unsigned acc = 0;
   for (long wb = first; wb + span <= n; wb += stride) {
     u32x4 v[U];
@@ -50,15 +76,15 @@ __global__ void __launch_bounds__(256) probe(const Streams S, long n, unsigned *
 #pragma unroll
     for (int r = 0; r < R; ++r)
 #pragma unroll
-      for (int u = 0; u < U; ++u) v[u] += __builtin_nontemporal_load(S.in[r] + wb + 64 * u + lane);
+      for (int u = 0; u < U; ++u) v[u] += load<LNT>(S.in[r] + wb + 64 * u + lane);
 #pragma unroll
     for (int w = 0; w < W; ++w)
 #pragma unroll
-      for (int u = 0; u < U; ++u) S.out[w][wb + 64 * u + lane] = v[u] + (unsigned)w;
+      for (int u = 0; u < U; ++u) store<SNT>(v[u] + (unsigned)w, S.out[w] + wb + 64 * u + lane);
 #pragma unroll
     for (int u = 0; u < U; ++u) acc += v[u].x ^ v[u].w;
   }
-  if (acc == 0x9e3779b9u) sink[0] = acc;  // keeps the reads alive
+  if (acc == 0x9e3779b9u) sink[0] = acc;  // keeps pure-read sweeps alive
 }
 
 static void check(hipError_t e, const char *what) {
@@ -68,75 +94,160 @@ static void check(hipError_t e, const char *what) {
   }
 }
 
-template <int R, int W, int U, int F = 0>
-static double run(const Streams &S, long n, int grid, unsigned *sink) {
-  if (F > 0) {  // one-shot: one block per 4 * 64 * U vectors, a multiple of F
-    const long blocks = n / (4L * 64 * U);
-    grid = int((blocks + F - 1) / F * F);
+struct Pools {
+  char *in, *out;
+  size_t in_bytes, out_bytes;
+  unsigned *sink;
+  int cus;
+};
+
+// Stream layouts: byte gap added between consecutive streams.
+constexpr long kGap[3] = {1280, 0, 65536 + 1280};
+const char *kGapName[3] = {"s1280", "s0", "s64k"};
+
+template <int R, int W, int U, bool LNT, bool SNT>
+static double run(const Pools &P, long n, int layout, int mode, int per_cu, int cap) {
+  Streams S;
+  std::memset(&S, 0, sizeof S);
+  const long stream_bytes = n * 16 + kGap[layout];
+  const long base = 2L << 20;
+  for (int i = 0; i < R; ++i) {
+    const size_t off = size_t(base + i * stream_bytes);
+    if (off + size_t(n) * 16 > P.in_bytes) return -1;
+    S.in[i] = reinterpret_cast<const u32x4 *>(P.in + off);
+  }
+  for (int i = 0; i < W; ++i) {
+    const size_t off = size_t(base + i * stream_bytes);
+    if (off + size_t(n) * 16 > P.out_bytes) return -1;
+    S.out[i] = reinterpret_cast<u32x4 *>(P.out + off);
+  }
+  const long span_blk = 4L * 64 * U;  // vectors per one-shot block
+  long grid = mode == 2 ? long(P.cus) * per_cu : n / span_blk;
+  if (mode != 2 && (n % span_blk != 0 || grid % 8 != 0)) return -1;
+  // cap: 0 = no reservation; else at most `cap` workgroups per CU through
+  // the LDS each one reserves (160 KiB per CU)
+  const size_t lds_of[5] = {0, 96 * 1024, 64 * 1024, 48 * 1024, 40 * 1024};
+  const size_t lds = lds_of[cap];
+  auto k = probe<R, W, U, LNT, SNT>;
+  if (lds > 64 * 1024 &&
+      hipFuncSetAttribute(reinterpret_cast<const void *>(k),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, int(lds)) != hipSuccess) {
+    (void)hipGetLastError();
+    return -1;  // this part cannot reserve that much LDS for one workgroup
   }
   hipEvent_t a, b;
   check(hipEventCreate(&a), "event");
   check(hipEventCreate(&b), "event");
-  hipLaunchKernelGGL((probe<R, W, U, F>), dim3(grid), dim3(256), 0, 0, S, n, sink);
+  hipLaunchKernelGGL(k, dim3(unsigned(grid)), dim3(256), lds, 0, S, n, mode, P.sink);
+  if (hipGetLastError() != hipSuccess) {  // launch refused (e.g. the LDS request): skip
+    check(hipEventDestroy(a), "event");
+    check(hipEventDestroy(b), "event");
+    return -1;
+  }
   check(hipEventRecord(a), "record");
-  const int iters = 4;
+  const int iters = 3;
   for (int it = 0; it < iters; ++it)
-    hipLaunchKernelGGL((probe<R, W, U, F>), dim3(grid), dim3(256), 0, 0, S, n, sink);
+    hipLaunchKernelGGL(k, dim3(unsigned(grid)), dim3(256), lds, 0, S, n, mode, P.sink);
+  check(hipGetLastError(), "launch");
   check(hipEventRecord(b), "record");
   check(hipEventSynchronize(b), "sync");
   float ms = 0;
   check(hipEventElapsedTime(&ms, a, b), "elapsed");
+  check(hipEventDestroy(a), "event");
+  check(hipEventDestroy(b), "event");
   return double(R + W) * n * 16.0 * iters / (ms * 1e-3) / 1e9;
 }
 
-template <int R, int W>
-static void mix(const char *name, const Streams &S, long n, unsigned *sink) {
-  const int grids[] = {2048, 16384, 65536};
-  double best = 0;
-  std::printf("%-6s", name);
-  for (int g : grids) {
-    const double a = run<R, W, 1>(S, n, g, sink), b = run<R, W, 4>(S, n, g, sink);
-    std::printf("  g%-5d U1 %6.0f U4 %6.0f", g, a, b);
-    best = a > best ? a : best;
-    best = b > best ? b : best;
+struct Best {
+  double gbs = 0;
+  char what[128] = "";
+};
+
+template <int R, int W, int U, bool LNT, bool SNT>
+static void shapes(const char *mix, const Pools &P, long n, Best &best) {
+  const char *pol = LNT ? (SNT ? "Lnt-Snt" : "Lnt-Spl") : (SNT ? "Lpl-Snt" : "Lpl-Spl");
+  for (int layout = 0; layout < 3; ++layout) {
+    struct Shape { int mode, per_cu, cap; const char *name; };
+    const Shape sh[] = {{0, 0, 0, "oneshot"},      {1, 0, 0, "oneshot-xcd"},
+                        {0, 0, 1, "oneshot-cap1"}, {1, 0, 1, "oneshot-xcd-cap1"},
+                        {0, 0, 2, "oneshot-cap2"}, {1, 0, 2, "oneshot-xcd-cap2"},
+                        {0, 0, 3, "oneshot-cap3"}, {1, 0, 3, "oneshot-xcd-cap3"},
+                        {0, 0, 4, "oneshot-cap4"}, {1, 0, 4, "oneshot-xcd-cap4"},
+                        {2, 8, 0, "persist8"}};
+    // the layout sweep only on the plain one-shot shape
+    for (const Shape &s : sh) {
+      if (layout != 0 && (s.mode != 0 || s.cap != 0)) continue;
+      const double g = run<R, W, U, LNT, SNT>(P, n, layout, s.mode, s.per_cu, s.cap);
+      if (g < 0) continue;
+      std::printf("%-7s %s U%d %-13s %-6s %7.0f GB/s\n", mix, pol, U, s.name, kGapName[layout], g);
+      if (g > best.gbs) {
+        best.gbs = g;
+        std::snprintf(best.what, sizeof best.what, "%s U%d %s %s", pol, U, s.name,
+                      kGapName[layout]);
+      }
+    }
   }
-  const double o14 = run<R, W, 4, 1>(S, n, 0, sink), o24 = run<R, W, 4, 2>(S, n, 0, sink),
-               o28 = run<R, W, 8, 2>(S, n, 0, sink);
-  std::printf("  one-shot F1 U4 %6.0f F2 U4 %6.0f F2 U8 %6.0f", o14, o24, o28);
-  for (double x : {o14, o24, o28}) best = x > best ? x : best;
-  std::printf("  | best %6.0f GB/s\n", best);
   std::fflush(stdout);
 }
 
-int main() {
-  // 64 input streams of 512 MiB (32 GiB), 8 output streams of 512 MiB (each
-  // larger than the 256 MB last-level cache);
-  // n vectors per stream, a multiple of every sweep span.
-  const long n = (512L << 20) / 16;
-  Streams S;
-  const long stagger = 1280 / 16;  // vectors
-  for (int i = 0; i < kMaxIn; ++i) {
-    u32x4 *p;
-    check(hipMalloc(&p, (n + kMaxIn * stagger) * 16), "malloc");
-    check(hipMemset(p, i, (n + kMaxIn * stagger) * 16), "memset");
-    S.in[i] = p + i * stagger;
+template <int R, int W, int U>
+static void policies(const char *mix, const Pools &P, long n, Best &best) {
+  shapes<R, W, U, true, true>(mix, P, n, best);
+  shapes<R, W, U, true, false>(mix, P, n, best);
+  shapes<R, W, U, false, true>(mix, P, n, best);
+  shapes<R, W, U, false, false>(mix, P, n, best);
+}
+
+template <int R, int W>
+static void mix(const char *name, const Pools &P, const std::vector<std::string> &want) {
+  if (!want.empty()) {
+    bool hit = false;
+    for (const auto &s : want) hit |= s == name;
+    if (!hit) return;
   }
-  for (int i = 0; i < kMaxOut; ++i) {
-    u32x4 *p;
-    check(hipMalloc(&p, (n + (kMaxIn + kMaxOut) * stagger) * 16), "malloc");
-    S.out[i] = p + (kMaxIn + i) * stagger;
-  }
-  unsigned *sink;
-  check(hipMalloc(&sink, 64), "malloc");
+  // about 6 GB per launch; n a multiple of 2 MiB / 16 (every span x 8 divides it)
+  const long unit = (2L << 20) / 16;
+  long n = long(6e9) / (long(R + W) * 16) / unit * unit;
+  if (n < unit) n = unit;
+  Best best;
+  policies<R, W, 1>(name, P, n, best);
+  policies<R, W, 2>(name, P, n, best);
+  policies<R, W, 4>(name, P, n, best);
+  policies<R, W, 8>(name, P, n, best);
+  std::printf("BEST %-7s R%d W%d %7.0f GB/s (%.1f%% of 8 TB/s)  %s\n", name, R, W, best.gbs,
+              best.gbs / 80.0, best.what);
+  std::fflush(stdout);
+}
+
+int main(int argc, char **argv) {
+  std::vector<std::string> want;
+  for (int i = 1; i < argc; ++i) want.emplace_back(argv[i]);
+  Pools P;
+  // the largest mix needs R * (n*16 + gap) <= in_bytes for every layout
+  P.in_bytes = size_t(7) << 30;
+  P.out_bytes = size_t(7) << 30;
+  check(hipMalloc(&P.in, P.in_bytes), "malloc in");
+  check(hipMalloc(&P.out, P.out_bytes), "malloc out");
+  check(hipMemset(P.in, 1, P.in_bytes), "memset");
+  check(hipMalloc(&P.sink, 64), "malloc sink");
   hipDeviceProp_t prop;
   check(hipGetDeviceProperties(&prop, 0), "props");
-  std::printf("device %s, %d CUs; GB/s per mix (grid, lane-vectors per wave sweep)\n",
-              prop.gcnArchName, prop.multiProcessorCount);
-  mix<1, 0>("R1W0", S, n, sink);
-  mix<0, 1>("R0W1", S, n, sink);
-  mix<1, 1>("R1W1", S, n, sink);
-  mix<16, 2>("R16W2", S, n, sink);
-  mix<8, 8>("R8W8", S, n, sink);
-  mix<64, 0>("R64W0", S, n, sink);
+  P.cus = prop.multiProcessorCount;
+  check(hipDeviceSynchronize(), "sync");
+  std::printf("device %s, %d CUs, LDS %zu B per workgroup / %zu B per CU; GB/s = (R+W) x n x 16 B "
+              "per launch / mean of 3 launches\n",
+              prop.gcnArchName, P.cus, size_t(prop.sharedMemPerBlock),
+              size_t(prop.maxSharedMemoryPerMultiProcessor));
+  mix<1, 0>("read", P, want);
+  mix<0, 1>("write", P, want);
+  mix<1, 1>("copy", P, want);
+  mix<16, 2>("norm16", P, want);
+  mix<8, 7>("upd", P, want);
+  mix<7, 7>("nd1", P, want);
+  mix<70, 7>("nd64", P, want);
+  mix<38, 7>("q8nd64", P, want);
+  check(hipFree(P.in), "free");
+  check(hipFree(P.out), "free");
+  check(hipFree(P.sink), "free");
   return 0;
 }
