@@ -128,7 +128,7 @@ def test_7p5b_nd64_windows():
     log(f"case {w.name}: n={n} n_d={w.n_d} steps={w.steps} (warm state, t0={w.t0})")
     g = GpuShard(w)
     g.init_state()
-    wins = windows(n, 10, 65536, seed=2)
+    wins = windows(n, 16, 65536, seed=2)
     ows = [OracleWindow(w, lo, hi - lo) for lo, hi in wins]
     for s in range(1, w.steps + 1):
         g.fill_grads(s)
@@ -147,7 +147,7 @@ def test_7p5b_zeropp_windows():
     log(f"case {w.name}: n={n} n_d={w.n_d} steps={w.steps} contrib block={w.contrib_block}")
     g = GpuShard(w)
     g.init_state()
-    wins = windows(n, 10, 65536, seed=5)
+    wins = windows(n, 16, 65536, seed=5)
     ows = [OracleWindow(w, lo, hi - lo) for lo, hi in wins]
     for s in range(1, w.steps + 1):
         g.fill_grads(s)
@@ -170,7 +170,7 @@ def test_13b_clip_int8_full_norm_and_windows():
     log(f"case {w.name}: n={n} n_d={w.n_d} steps={steps} clip={w.max_norm} block={w.quant_block}")
     g = GpuShard(w)
     g.init_state()
-    wins = windows(n, 8, 65536, seed=3)
+    wins = windows(n, 16, 65536, seed=3)
     ows = [OracleWindow(w, lo, hi - lo) for lo, hi in wins]
     for s in range(1, steps + 1):
         g.fill_grads(s)
@@ -198,7 +198,7 @@ def test_13b_stage0_nd1_windows():
     bounds += [(1 << 31) - 4096, (1 << 32) - 4096, n // 2]
     g = GpuShard(w)
     g.init_state()
-    wins = windows(n, 14, 16384, seed=4, extra=tuple(bounds))
+    wins = windows(n, 16, 65536, seed=4, extra=tuple(bounds))
     ows = [OracleWindow(w, lo, hi - lo) for lo, hi in wins]
     for s in range(1, w.steps + 1):
         g.fill_grads(s)
