@@ -16,8 +16,10 @@ whole step's GB/s both over the bytes the path moves and over the pages'
 modelled (2 N_d + 26 [+ int8 out]) B/param, the same figures for the other
 full-size workloads timed in the same run (``configs``: the 7.5B-parameter
 model at N_d = 64 with bf16 and with int8 contributions, the 13B stage-0
-flat buffer), and the CPU oracle's rate on a bounded sample of the default
-workload.
+flat buffer), each launch's GB/s as a fraction of what the stream probe
+(``tests/native/hbm_probe``, run first as a child process) reaches at best
+for the same read:write mix (``ceiling``), and the CPU oracle's rate on a
+bounded sample of the default workload.
 """
 
 from __future__ import annotations
@@ -151,6 +153,74 @@ def measured_traffic(w, kernel: str) -> float | None:
     if rec != sha:
         return None
     return tr.get(kernel)
+
+
+PROBE = os.path.join(ROOT, "tests", "native", "hbm_probe")
+
+
+def probe_mix(w, kernel: str, spill: bool) -> str | None:
+    """The stream probe's mix with this launch's read:write traffic, if it
+    has one: the norm pass at N_d = 16, the clipped update that reads the
+    spill, and the unclipped updates at N_d = 1 and 64 (bf16 or int8 rows)."""
+    if kernel == "gnorm":
+        return "norm16" if (w.n_d == 16 and not w.contrib_block and spill) else None
+    if w.max_norm > 0:
+        return "upd" if spill else None
+    if w.contrib_block:
+        return "q8nd64" if w.n_d == 64 else None
+    return {1: "nd1", 64: "nd64"}.get(w.n_d)
+
+
+def probe_ceilings(mixes: list[str]) -> dict | None:
+    """Run the stream probe (a child process, before this process allocates
+    anything on the GPU) over every access shape it sweeps for the given
+    mixes; return each mix's best GB/s and the shape that reached it."""
+    import subprocess
+
+    if not mixes or not os.access(PROBE, os.X_OK):
+        return None
+    _eprint(f"[bench] HBM stream probe, mixes {' '.join(mixes)}")
+    try:
+        out = subprocess.run([PROBE, *mixes], capture_output=True, text=True, timeout=600)
+    except (OSError, subprocess.SubprocessError) as e:
+        _eprint(f"[bench] probe failed: {e}")
+        return None
+    if out.returncode != 0:
+        _eprint(f"[bench] probe exited {out.returncode}: {out.stderr.strip()[-300:]}")
+        return None
+    best = parse_probe_best(out.stdout)
+    for mix, b in best.items():
+        _eprint(f"[bench] probe best {mix}: {b['best_GBps']:.0f} GB/s, {b['shape']}")
+    return best or None
+
+
+def parse_probe_best(text: str) -> dict:
+    """The probe's per-mix summary lines ('BEST <mix> R<r> W<w> <GB/s> GB/s
+    (..) <shape>') as {mix: {reads, writes, best_GBps, shape}}."""
+    import re
+
+    best = {}
+    for line in text.splitlines():
+        m = re.match(r"BEST\s+(\S+)\s+R(\d+)\s+W(\d+)\s+(\d+) GB/s .*?\)\s+(.*)$", line)
+        if m:
+            best[m.group(1)] = {"reads": int(m.group(2)), "writes": int(m.group(3)),
+                                "best_GBps": float(m.group(4)), "shape": m.group(5).strip()}
+    return best
+
+
+def against_probe(w, r: dict, spill: bool, best: dict | None) -> dict | None:
+    """Each timed launch's GB/s as a fraction of the probe's best for the
+    same read:write mix."""
+    if not best:
+        return None
+    out = {}
+    for k, pk in r["per_kernel"].items():
+        mix = probe_mix(w, k, spill)
+        if mix in best:
+            out[k] = {"mix": mix, "achieved_GBps": pk["GBps"],
+                      "probe_best_GBps": best[mix]["best_GBps"],
+                      "frac_of_probe": round(pk["GBps"] / best[mix]["best_GBps"], 4)}
+    return out or None
 
 
 def bench_dequant(w, args) -> int:
@@ -549,6 +619,9 @@ def main() -> int:
     ap.add_argument("--extra-configs", default="7.5B-nd64,7.5B-nd64-zeropp,13B-nd1-stage0",
                     help="other workloads timed in the same run and reported under 'configs'")
     ap.add_argument("--no-extra-configs", action="store_true")
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="skip the HBM stream probe that gives each kernel's read:write-mix "
+                         "ceiling")
     ap.add_argument("--no-spill", action="store_true",
                     help="clipped steps re-read the contributions instead of the fp32 spill")
     ap.add_argument("--dequant", action="store_true",
@@ -614,6 +687,17 @@ def main() -> int:
     if args.bucket:
         per = -(-int(args.bucket) // w.n_d)
         bucket_len = -(-per // 512) * 512
+    extra_names = [] if (args.no_extra_configs or bucket_len) else \
+        [c for c in args.extra_configs.split(",") if c and c != w.name]
+    best = None
+    if not args.no_ceiling:
+        mixes = []
+        for wx, sp in [(w, spill)] + [(S.by_name(c), True) for c in extra_names]:
+            for k in kernel_bytes(wx, sp):
+                mx = probe_mix(wx, k, sp)
+                if mx and mx not in mixes:
+                    mixes.append(mx)
+        best = probe_ceilings(mixes)
     head = measure(w, args, spill, bucket_len)
     n = w.shard_len
     kb = head["kb"]
@@ -621,10 +705,11 @@ def main() -> int:
     # the other full-size workloads the >= 80% target is judged on, timed the
     # same way in the same run (each allocated, timed and freed in turn)
     extra = {}
-    if not args.no_extra_configs and not bucket_len:
-        for name in [c for c in args.extra_configs.split(",") if c and c != w.name]:
-            wx = S.by_name(name)
-            extra[wx.name] = summary(wx, measure(wx, args, True, 0))
+    for name in extra_names:
+        wx = S.by_name(name)
+        rx = measure(wx, args, True, 0)
+        extra[wx.name] = summary(wx, rx)
+        extra[wx.name]["ceiling"] = against_probe(wx, rx, True, best)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -664,6 +749,11 @@ def main() -> int:
         "roofline": {"bound": "hbm", "kernel": kernel_names[dominant], "achieved": ach,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
                      "traffic": traffic},
+        "ceiling": None if best is None else {
+            "probe": "tests/native/hbm_probe, run in this bench: best over its access shapes "
+                     "for each launch's read:write mix",
+            "mixes": best,
+            "kernels": against_probe(w, head, spill, best)},
         "configs": extra or None,
         "cpu_baseline": cpu,
     }
