@@ -85,7 +85,7 @@ def cpu_baseline(w, target_s: float = 12.0, max_n: int = 1 << 27) -> dict:
     GPU's share of the host has; ``cores`` is the threads used, ``host`` the
     machine's own count and CPU model); clipping uses the norm of the
     sample.  Also the plain single-thread rate on a 2^22-element sample
-    (about 4 s)."""
+    (about 4 s).  Both also as the pages' modelled bytes per second."""
     try:
         threads = max(1, min(16, len(os.sched_getaffinity(0))))
     except AttributeError:
@@ -94,13 +94,16 @@ def cpu_baseline(w, target_s: float = 12.0, max_n: int = 1 << 27) -> dict:
     steps, spent = _time_oracle(w, n, threads, target_s)
     n1 = min(w.shard_len, 1 << 22)
     steps1, spent1 = _time_oracle(w, n1, 1, target_s / 3)
-    return {"value": n * steps / spent, "unit": "params/s", "cores": threads, "kind": "oracle",
+    rate, rate1 = n * steps / spent, n1 * steps1 / spent1
+    return {"value": rate, "unit": "params/s", "cores": threads, "kind": "oracle",
+            "modelled_GBps": round(rate * modelled_bytes(w) / 1e9, 3),
             "host": host_cpu(),
             "sample": f"first {n} of {w.shard_len} shard elements of {w.name}, {steps} steps "
                       f"on resident inputs (norm over the sample), {threads} threads, "
                       f"{spent:.1f} s",
             "seconds": round(spent, 3),
-            "single_thread": {"value": n1 * steps1 / spent1, "unit": "params/s", "cores": 1,
+            "single_thread": {"value": rate1, "unit": "params/s", "cores": 1,
+                              "modelled_GBps": round(rate1 * modelled_bytes(w) / 1e9, 3),
                               "sample": f"first {n1} elements, {steps1} steps, "
                                         f"{spent1:.1f} s"}}
 
@@ -619,6 +622,10 @@ def main() -> int:
     ap.add_argument("--extra-configs", default="7.5B-nd64,7.5B-nd64-zeropp,13B-nd1-stage0",
                     help="other workloads timed in the same run and reported under 'configs'")
     ap.add_argument("--no-extra-configs", action="store_true")
+    ap.add_argument("--cold-cache", type=int, default=0, metavar="MIB",
+                    help="write a MIB-MiB scratch buffer between timed steps, so that no step "
+                         "finds the previous one's data in the caches; ms_per_step and value "
+                         "then come from the HIP events around the step's calls")
     ap.add_argument("--no-ceiling", action="store_true",
                     help="skip the HBM stream probe that gives each kernel's read:write-mix "
                          "ceiling")
@@ -740,6 +747,7 @@ def main() -> int:
                    "max_norm": w.max_norm, "weight_decay": w.weight_decay,
                    "quant_block": w.quant_block, "grad_spill": bool(spill and w.max_norm > 0),
                    "bucket_len": bucket_len or None,
+                   "cold_cache_MiB": args.cold_cache or None,
                    "bucket_streams": args.bucket_streams if bucket_len else None,
                    "storage": {"contributions": "int8" if w.contrib_block else "bf16",
                                "state": "fp32", "params_out": "bf16",
@@ -851,12 +859,18 @@ def measure(w, args, spill: bool, bucket_len: int) -> dict:
     torch.cuda.synchronize()
 
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    cold = args.cold_cache
+    scratch = torch.empty((cold << 20) // 4, dtype=torch.float32, device=g.master.device) \
+        if cold else None
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
+        if cold:
+            scratch.fill_(float(i))  # outside the step's events
         one_step(args.warmup + 1 + i, evs[i])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    del scratch
     _eprint(f"[bench] timed {args.steps} steps in {elapsed * 1e3:.2f} ms")
 
     dur = {"step": [e[1].elapsed_time(e[2]) for e in evs]}
@@ -874,6 +888,9 @@ def measure(w, args, spill: bool, bucket_len: int) -> dict:
         _eprint(f"[bench] {w.name} {k}: {ms:.4f} ms, {kb[k]:.3f} B/param, {gbs:.1f} GB/s "
                 f"({100 * gbs / HBM_PEAK_GBS:.1f}% of 8 TB/s)")
     ms_step = elapsed * 1e3 / args.steps
+    if cold:  # the wall clock would include the scratch writes
+        first = 0 if g.clip else 1
+        ms_step = sum(e[first].elapsed_time(e[2]) for e in evs) / len(evs)
     g.free()
     del g
     torch.cuda.empty_cache()
