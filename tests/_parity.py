@@ -33,7 +33,22 @@ def f32_close(name: str, gpu: np.ndarray, orc: np.ndarray, rtol: float = RTOL,
     same = gpu.view(np.uint32) == orc.view(np.uint32)
     with np.errstate(divide="ignore", invalid="ignore"):
         rel = np.where(o != 0, np.abs(g - o) / np.abs(o), 0.0)
-    return {"bitwise": float(same.mean()), "max_rel": float(np.nanmax(rel)) if rel.size else 0.0}
+        rtol_only = int(((np.abs(g - o) > rtol * np.abs(o)) & ~both_nan).sum())
+    ulps = np.abs(_f32_order(gpu) - _f32_order(orc))
+    ulps[both_nan] = 0
+    return {"bitwise": float(same.mean()), "max_rel": float(np.nanmax(rel)) if rel.size else 0.0,
+            # diagnostics, not gates: binary32 ulps apart, and the elements
+            # the relative bound alone (without the 1e-9 floor) would reject
+            "ulp_hist": {"0": int((ulps == 0).sum()), "1": int((ulps == 1).sum()),
+                         "2+": int((ulps >= 2).sum())},
+            "rtol_only_out": rtol_only}
+
+
+def _f32_order(x: np.ndarray) -> np.ndarray:
+    """binary32 patterns mapped to integers in the order of their values
+    (+0 and -0 both to 0), so that a difference counts ulps."""
+    b = x.view(np.uint32).astype(np.int64)
+    return np.where(b & 0x80000000, -(b & 0x7FFFFFFF), b)
 
 
 def _bf16_order(b: np.ndarray) -> np.ndarray:
