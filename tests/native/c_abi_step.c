@@ -3,7 +3,12 @@
  * C ABI (include/zero_shard.h) and the HIP runtime API, with no Python and
  * no PyTorch in the process.  Used by tests/test_gpu_c_abi.py.
  *
- * Usage: c_abi_step IN OUT
+ * Usage: c_abi_step IN OUT [graph]
+ * With "graph" the step is captured once into a HIP graph and replayed at
+ * every step: the allocation-free norm pass (zero_shard_gnorm_noalloc, no
+ * spill) and zero_shard_step_dev, which re-reads the contributions and takes
+ * lr, lr*wd and the bias corrections from a device array the program
+ * refreshes (zero_shard_step_consts) before each replay, outside the graph.
  * IN (little-endian, packed):
  *   int64 n; int32 n_d; int32 quant_block; int32 steps;
  *   float lr, weight_decay, max_norm;
@@ -46,10 +51,11 @@ static int read_all(FILE *f, void *p, size_t bytes) {
 }
 
 int main(int argc, char **argv) {
-  if (argc != 3) {
-    fprintf(stderr, "usage: %s IN OUT\n", argv[0]);
+  if (argc != 3 && !(argc == 4 && strcmp(argv[3], "graph") == 0)) {
+    fprintf(stderr, "usage: %s IN OUT [graph]\n", argv[0]);
     return 2;
   }
+  const int graph = argc == 4;
   FILE *in = fopen(argv[1], "rb");
   if (!in) {
     perror(argv[1]);
@@ -122,19 +128,54 @@ int main(int argc, char **argv) {
   d.q_scales = scales;
   d.gbar_ws = gbar;
   d.stream = stream;
+  if (graph) d.gbar_ws = NULL;  /* the captured step re-reads the contributions */
   zs_handle *h = NULL;
   ZS_OK_(zero_shard_init(&d, &h));
-  for (int32_t s = 0; s < steps; ++s) {
-    for (int k = 0; k < nd; ++k)
-      HIP_OK(hipMemcpyAsync(rows[k], h_rows + ((size_t)s * nd + k) * n, b16,
-                            hipMemcpyHostToDevice, stream));
-    const zs_bf16 *const *c = (const zs_bf16 *const *)rows;
-    if (max_norm > 0.0f) {
-      ZS_OK_(zero_shard_gnorm(h, c, sumsq + s));
-      ZS_OK_(zero_shard_step(h, NULL, lr, s + 1, sumsq + s));  /* reads the spill */
-    } else {
-      ZS_OK_(zero_shard_step(h, c, lr, s + 1, NULL));
+  const zs_bf16 *const *c = (const zs_bf16 *const *)rows;
+  if (!graph) {
+    for (int32_t s = 0; s < steps; ++s) {
+      for (int k = 0; k < nd; ++k)
+        HIP_OK(hipMemcpyAsync(rows[k], h_rows + ((size_t)s * nd + k) * n, b16,
+                              hipMemcpyHostToDevice, stream));
+      if (max_norm > 0.0f) {
+        ZS_OK_(zero_shard_gnorm(h, c, sumsq + s));
+        ZS_OK_(zero_shard_step(h, NULL, lr, s + 1, sumsq + s));  /* reads the spill */
+      } else {
+        ZS_OK_(zero_shard_step(h, c, lr, s + 1, NULL));
+      }
     }
+  } else {
+    double *consts_dev, *ssq;
+    double *consts_host = (double *)malloc((size_t)steps * 4 * sizeof(double));
+    if (!consts_host) return 1;
+    HIP_OK(hipMalloc((void **)&consts_dev, 4 * sizeof(double)));
+    HIP_OK(hipMalloc((void **)&ssq, sizeof(double)));
+    for (int32_t s = 0; s < steps; ++s)
+      ZS_OK_(zero_shard_step_consts(&d, lr, s + 1, consts_host + 4 * (size_t)s));
+    hipGraph_t g;
+    hipGraphExec_t exec;
+    HIP_OK(hipStreamBeginCapture(stream, hipStreamCaptureModeGlobal));
+    if (max_norm > 0.0f) ZS_OK_(zero_shard_gnorm_noalloc(&d, c, ssq));
+    ZS_OK_(zero_shard_step_dev(h, c, consts_dev, max_norm > 0.0f ? ssq : NULL));
+    HIP_OK(hipStreamEndCapture(stream, &g));
+    HIP_OK(hipGraphInstantiate(&exec, g, NULL, NULL, 0));
+    for (int32_t s = 0; s < steps; ++s) {
+      for (int k = 0; k < nd; ++k)
+        HIP_OK(hipMemcpyAsync(rows[k], h_rows + ((size_t)s * nd + k) * n, b16,
+                              hipMemcpyHostToDevice, stream));
+      HIP_OK(hipMemcpyAsync(consts_dev, consts_host + 4 * (size_t)s, 4 * sizeof(double),
+                            hipMemcpyHostToDevice, stream));
+      HIP_OK(hipGraphLaunch(exec, stream));
+      if (max_norm > 0.0f)
+        HIP_OK(hipMemcpyAsync(sumsq + s, ssq, sizeof(double), hipMemcpyDeviceToDevice,
+                              stream));
+    }
+    HIP_OK(hipStreamSynchronize(stream));
+    HIP_OK(hipGraphExecDestroy(exec));
+    HIP_OK(hipGraphDestroy(g));
+    HIP_OK(hipFree(consts_dev));
+    HIP_OK(hipFree(ssq));
+    free(consts_host);
   }
   HIP_OK(hipStreamSynchronize(stream));
 

@@ -1,7 +1,9 @@
 """The boundary from plain C: tests/native/c_abi_step (built by
 __graft_entry__.build(); no Python or PyTorch in its process) allocates with
 hipMalloc, calls zero_shard_init / zero_shard_gnorm / zero_shard_step /
-zero_shard_free, and writes its outputs; they are compared with the oracle
+zero_shard_free (or captures zero_shard_gnorm_noalloc and
+zero_shard_step_dev into one HIP graph and replays it), and writes its
+outputs; they are compared with the oracle
 on the same seeded inputs, to the parity tolerances."""
 
 from __future__ import annotations
@@ -31,12 +33,17 @@ def _need_gpu():
         pytest.skip("no GPU")
 
 
+@pytest.mark.parametrize("mode", ["eager", "graph"])
 @pytest.mark.parametrize("name,n,nd,qb,clip,steps", [
     ("tiny-zero1", 4099, 4, 256, 0.0, 3),
     ("13B-nd16-clip-int8", 100_003, 16, 256, 0.05, 3),
     ("gpt2-small-flat", 65_536 + 7, 8, 0, 0.0, 2),
 ])
-def test_c_program_matches_oracle(tmp_path, name, n, nd, qb, clip, steps):
+def test_c_program_matches_oracle(tmp_path, name, n, nd, qb, clip, steps, mode):
+    """eager: gnorm (with the spill) and step at every step; graph: one HIP
+    graph captured from C (allocation-free norm pass without a spill, the
+    step re-reading the contributions with its constants read on the
+    device), replayed at every step."""
     if not os.path.exists(EXE):
         pytest.fail("tests/native/c_abi_step is not built (run __graft_entry__.build())")
     w = S.by_name(name)
@@ -53,9 +60,10 @@ def test_c_program_matches_oracle(tmp_path, name, n, nd, qb, clip, steps):
             f.write(a.tobytes())
         for r in rows:
             f.write(np.ascontiguousarray(r).tobytes())
-    print(f"case c abi {name} n={n} nd={nd} qb={qb} clip={clip}", flush=True)
+    print(f"case c abi {mode} {name} n={n} nd={nd} qb={qb} clip={clip}", flush=True)
     sys.stdout.flush()
-    r = subprocess.run([EXE, str(src), str(dst)], capture_output=True, text=True, timeout=120)
+    argv = [EXE, str(src), str(dst)] + (["graph"] if mode == "graph" else [])
+    r = subprocess.run(argv, capture_output=True, text=True, timeout=120)
     assert r.returncode == 0, r.stderr
     out = np.fromfile(dst, dtype=np.uint8)
     off = 0
