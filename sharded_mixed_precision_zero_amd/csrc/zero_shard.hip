@@ -7,8 +7,10 @@
 //    128-bit load, each fp32 state array two, the bf16 output one 128-bit
 //    store; a wave64 touches 1 KiB of every row per access, fully coalesced;
 //  * the rank-order sum of the bf16 contributions runs in binary64 registers
-//    (full-rate fp64 on CDNA), exact for these addends; the average is
-//    rounded once to binary32, the precision the reduce-scatter delivers;
+//    (binary64 adds issue at the unpacked-binary32 rate on CDNA4, half its
+//    packed peak), exact unless the addends span some 45 binades; the
+//    average is rounded once to binary32, the precision the reduce-scatter
+//    delivers;
 //  * rows are loaded in groups of kRowGroup so that many 16-byte loads per
 //    lane are in flight while the sum keeps its fixed k order;
 //  * the AdamW update runs in binary64 from the binary32 state with every
