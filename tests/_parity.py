@@ -40,7 +40,7 @@ def f32_close(name: str, gpu: np.ndarray, orc: np.ndarray, rtol: float = RTOL,
     ulps = np.abs(_f32_order(gs) - _f32_order(os_))
     ulps[both_nan] = 0
     return {"bitwise": 1.0 - idx.size / max(1, gpu.size),
-            "max_rel": float(np.nanmax(rel)) if rel.size else 0.0,
+            "max_rel": float(np.nanmax(rel)) if (~np.isnan(rel)).any() else 0.0,
             # diagnostics, not gates: binary32 ulps apart, and the elements
             # the relative bound alone (without the 1e-9 floor) would reject
             "ulp_hist": {"0": int(gpu.size - idx.size + (ulps == 0).sum()),
