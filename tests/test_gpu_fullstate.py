@@ -1,4 +1,4 @@
-"""Full final state at full size: after two steps of a large workload the
+"""Full final state at full size: after the steps of a large workload the
 GPU's whole shard (master, m, v, the bf16 copy, int8 codes and scales) is
 compared with the oracle's, chunk by chunk, to the parity tolerances.  The
 window tests follow more steps on sampled windows; this covers every
@@ -101,26 +101,31 @@ class FullOracle:
         return None
 
 
-@pytest.mark.parametrize("name", ["7.5B-nd64", "7.5B-nd64-zeropp", "13B-nd16-clip-int8"])
-def test_full_final_state_after_two_steps(name):
+def run_and_compare(name: str, steps: int) -> None:
+    """Steps 1..steps of workload `name` on the GPU and in the oracle (fresh
+    seeded gradients every step, S compared at every clipped step), then
+    the whole final shard compared chunk by chunk."""
+    import time
+
     import torch
 
     w = S.by_name(name)
     n = w.shard_len
-    log(f"case full state {name}: n={n} n_d={w.n_d}")
+    log(f"case full state {name}: n={n} n_d={w.n_d}, {steps} steps")
     g = GpuShard(w)
     g.init_state()
+    t0 = time.time()
     with ThreadPoolExecutor(max_workers=8) as pool:
         orc = FullOracle(w, pool)
-        for s in (1, 2):
+        for s in range(1, steps + 1):
             g.fill_grads(s)
             g.step(s)
             total = orc.step(s)
             if total is not None:
                 torch.cuda.synchronize()
                 got = float(g.sumsq.item())
-                assert abs(got - total) <= P.sumsq_tolerance(n, total), (got, total)
-            log(f"  step {s} done")
+                assert abs(got - total) <= P.sumsq_tolerance(n, total), (s, got, total)
+            log(f"  step {s} done ({time.time() - t0:.0f} s)")
     torch.cuda.synchronize()
     worst = 0
     for j, (lo, hi) in enumerate(orc.chunks):
@@ -140,9 +145,18 @@ def test_full_final_state_after_two_steps(name):
                 c2, _ = O.quant_int8(got["p"], w.quant_block)
                 blk = np.repeat(diff, w.quant_block)[:hi - lo]
                 assert np.array_equal(got["codes"][blk], c2[blk])
-    log(f"  all {len(orc.chunks)} chunks within tolerance; int8 blocks with differing input "
-        f"in a chunk: at most {worst}")
+    log(f"  all {len(orc.chunks)} chunks within tolerance after {steps} steps; int8 blocks "
+        f"with differing input in a chunk: at most {worst}")
     g.free()
+
+
+@pytest.mark.parametrize("name,steps", [("7.5B-nd64", 2), ("7.5B-nd64-zeropp", 2),
+                                        ("13B-nd16-clip-int8", 10)])
+def test_full_final_state(name, steps):
+    """The 13B clipped workload through all its 10 steps (about a minute);
+    the 7.5B workloads after 2 of their 50 (all 50 take 2.5 minutes each:
+    tests/test_gpu_long_parity.py)."""
+    run_and_compare(name, steps)
 
 
 def test_13b_stage0_full_final_state_streamed():
