@@ -159,11 +159,11 @@ def test_full_final_state(name, steps):
     run_and_compare(name, steps)
 
 
-def test_13b_stage0_full_final_state_streamed():
+def stage0_streamed(steps: int) -> None:
     """The 13B stage-0 flat buffer (12,851,609,600 elements, N_d = 1,
-    unclipped) after two steps: every element against the oracle.  An
+    unclipped) after `steps` steps: every element against the oracle.  An
     unclipped step is elementwise, so each 2^24-element chunk is regenerated
-    from its seeds (initial state, both steps' contributions) and stepped by
+    from its seeds (initial state, every step's contributions) and stepped by
     the oracle on its own, on a pool of host threads, then compared with the
     GPU's chunk; host memory stays bounded by the chunks in flight."""
     import time
@@ -172,21 +172,21 @@ def test_13b_stage0_full_final_state_streamed():
 
     w = S.by_name("13B-nd1-stage0")
     n = w.shard_len
-    log(f"case full state streamed {w.name}: n={n} (205.6 GB resident)")
+    log(f"case full state streamed {w.name}: n={n} (205.6 GB resident), {steps} steps")
     g = GpuShard(w)
     g.init_state()
-    for s in (1, 2):
+    for s in range(1, steps + 1):
         g.fill_grads(s)
         g.step(s)
     torch.cuda.synchronize()
     chunks = [(lo, min(n, lo + CHUNK)) for lo in range(0, n, CHUNK)]
     hyper = {s: O.Hyper(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps,
-                        weight_decay=w.weight_decay, t=w.t_of(s)) for s in (1, 2)}
+                        weight_decay=w.weight_decay, t=w.t_of(s)) for s in range(1, steps + 1)}
 
     def one(j):
         lo, hi = chunks[j]
         master, m, v = S.host_state(w, lo, hi - lo)
-        for s in (1, 2):
+        for s in range(1, steps + 1):
             out = O.step(list(S.host_contrib(w, s, lo, hi - lo)), master, m, v, hyper[s])
         got = g.host(lo, hi)
         nm = f"{w.name} [{lo},{hi})"
@@ -203,6 +203,11 @@ def test_13b_stage0_full_final_state_streamed():
             bitwise.append(b)
             if i % 64 == 0 or i == len(chunks):
                 log(f"  {i}/{len(chunks)} chunks within tolerance ({time.time() - t0:.0f} s)")
-    log(f"  every element of the 13B stage-0 buffer within tolerance; master bitwise "
-        f"fraction min {min(bitwise):.6f}")
+    log(f"  every element of the 13B stage-0 buffer within tolerance after {steps} steps; "
+        f"master bitwise fraction min {min(bitwise):.6f}")
     g.free()
+
+
+def test_13b_stage0_full_final_state_streamed():
+    """Two of the buffer's 20 steps (all 20: tests/test_gpu_long_parity.py)."""
+    stage0_streamed(2)

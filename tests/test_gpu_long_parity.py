@@ -1,9 +1,10 @@
-"""The whole final shard after all 50 steps of the 7.5B workloads (bf16 and
-int8 contributions), against the oracle chunk by chunk.  About 2.5 minutes
-each on one MI355X machine with 16 host cores, so it runs only when asked for
-(ZS_LONG_PARITY=1); the default GPU suite compares their whole shard after
-two steps and 16 windows at every step, and the 13B clipped workload's
-whole shard after all its 10 steps."""
+"""The whole final shard after all the steps of the full-size workloads the
+default GPU suite follows only on windows past step 2: the 7.5B workloads
+(bf16 and int8 contributions) after all 50 steps, about 2.5 minutes each,
+and the 13B stage-0 buffer after all 20, about 9 minutes, on one MI355X machine
+with 16 host cores.  So it runs only when asked for (ZS_LONG_PARITY=1); the
+default suite compares their whole shard after two steps and 16 windows at
+every step, and the 13B clipped workload's whole shard after all 10 steps."""
 
 from __future__ import annotations
 
@@ -12,7 +13,7 @@ import os
 import pytest
 
 import seeded_inputs as S
-from tests.test_gpu_fullstate import run_and_compare
+from tests.test_gpu_fullstate import run_and_compare, stage0_streamed
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(os.environ.get("ZS_LONG_PARITY") != "1",
@@ -33,3 +34,7 @@ def _gpu_cleanup():
 @pytest.mark.parametrize("name", ["7.5B-nd64", "7.5B-nd64-zeropp"])
 def test_full_final_state_after_every_step(name):
     run_and_compare(name, S.by_name(name).steps)
+
+
+def test_13b_stage0_full_final_state_after_every_step():
+    stage0_streamed(S.by_name("13B-nd1-stage0").steps)
