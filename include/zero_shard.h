@@ -127,8 +127,9 @@ int zero_shard_init(const zs_desc *d, zs_handle **out);
  * S_local = sum_i gbar_i^2 (binary64), reduced over a grid fixed by the
  * shard length, in a fixed order, with no atomics (same inputs => same
  * bits).  contrib is a HOST array of n_d device pointers, contrib[k] =
- * rank k's bf16 gradient for this shard (shard-local index).  Writes S_local to *sumsq_dev (device,
- * one double).  With gbar_ws set, also stores gbar there for the next step.
+ * rank k's bf16 gradient for this shard (shard-local index).  Writes
+ * S_local to *sumsq_dev (device, one double).  With gbar_ws set, also
+ * stores gbar there for the next step.
  * Summing S_local over the shards (one scalar all-reduce across ranks) gives
  * the S that zero_shard_step takes.  Errors: ZS_EINVAL, ZS_EALIGN, ZS_EHIP,
  * ZS_ESTATE. */
