@@ -787,3 +787,61 @@ def test_adam_no_bias_correction_closed_forms():
     big = np.abs(g64) >= 1e-4  # eps negligible next to sqrt(1 - b2) |g|
     ratio = (u1 - theta0).astype(np.float64)[big] / (c1 - theta0).astype(np.float64)[big]
     assert np.allclose(ratio, (1 - b1) / np.sqrt(1 - b2), rtol=5e-3)
+
+
+# ------------------------------------------------------ non-finite inputs
+
+def test_nonfinite_propagate_per_ieee_through_reduce_and_adam():
+    """Reading 16 (non-finite values propagate, no step is skipped), worked by
+    hand: a NaN contribution makes that element's average, m, v and theta
+    NaN; +inf gives m = v = +inf and theta = NaN (lr * inf / (inf + eps));
+    +inf and -inf in one element give NaN; every other element is the
+    finite step."""
+    inf, nan = np.float32(np.inf), np.float32(np.nan)
+    one = np.float32(1.0)
+    r0 = np.array([nan, inf, inf, one, one], np.float32)
+    r1 = np.array([one, one, -inf, one, one], np.float32)
+    rows = [O.f32_to_bf16(r0), O.f32_to_bf16(r1)]
+    g = O.reduce_average(rows)
+    assert np.isnan(g[0]) and g[1] == inf and np.isnan(g[2])
+    assert g[3] == 1.0 and g[4] == 1.0
+    n = g.size
+    master = np.full(n, 0.5, np.float32)
+    m = np.zeros(n, np.float32)
+    v = np.zeros(n, np.float32)
+    h = O.Hyper(lr=1e-3, weight_decay=0.0, t=1)
+    O.adam(master, m, v, g, 1.0, h)
+    assert np.isnan(master[0]) and np.isnan(m[0]) and np.isnan(v[0])
+    assert m[1] == inf and v[1] == inf and np.isnan(master[1])
+    assert np.isnan(master[2]) and np.isnan(m[2])
+    # the finite elements: first step from zero state, -lr g/(|g| + eps),
+    # with lr and eps the binary32 values widened
+    lr, eps = float(np.float32(1e-3)), float(np.float32(1e-8))
+    want = np.float32(0.5 - lr * 1.0 / (1.0 + eps))
+    assert np.all(master[3:] == want)
+
+
+def test_quant_blocks_with_nonfinite_values():
+    """Reading 7's rule for non-finite quotients: a block holding a NaN gets
+    a NaN scale (the absmax propagates the NaN) and codes 0; a block holding
+    +inf (and no NaN) gets scale +inf and codes 0 (finite / inf = 0, inf /
+    inf is NaN -> 0); a finite block next to them is quantized as usual."""
+    block = 4
+    vals = np.array([1.0, np.nan, -2.0, 0.5,      # NaN block
+                     np.inf, 3.0, -1.0, 0.25,     # inf block
+                     127.0, -63.5, 2.5, 0.0],     # finite: scale 1, ties to even
+                    np.float32)
+    codes, scales = O.quant_int8(O.f32_to_bf16(vals), block)
+    assert np.isnan(scales[0]) and np.all(codes[0:4] == 0)
+    assert scales[1] == np.inf and np.all(codes[4:8] == 0)
+    assert scales[2] == 1.0
+    assert codes[8:12].tolist() == [127, -64, 2, 0]
+
+
+def test_clip_coef_at_nonfinite_sums():
+    """coef = min(1, max_norm / (sqrt(S) + 1e-6)): a NaN S gives NaN (no
+    silent skip), S = +inf gives 0, S = 0 gives 1 (max_norm / 1e-6 >= 1)."""
+    assert np.isnan(O.clip_coef(float("nan"), 1.0))
+    assert O.clip_coef(float("inf"), 1.0) == 0.0
+    assert O.clip_coef(0.0, 1.0) == 1.0
+    assert O.clip_coef(4.0, 1.0) == 1.0 / (2.0 + 1e-6)
