@@ -139,6 +139,24 @@ def test_nonfinite_propagates_per_element_unclipped():
     g.free()
 
 
+@pytest.mark.parametrize("bits,name", [(0x7F80, "+inf"), (0xFF80, "-inf")])
+def test_infinite_contribution_unclipped_quantized(bits, name):
+    """An infinite contribution element: m and v infinite, theta NaN at that
+    element only (lr * inf / inf); the int8 block holding that NaN gets a NaN
+    scale and codes 0 (the oracle's rule, compared element by element by
+    _run_pair), every other block its finite quantization."""
+    log(f"case {name} in rank 1, element 777, unclipped, block 128")
+    w = _variant("tiny-zero1", quant_block=128)
+    g, ow = _run_pair(w, 4099, 2, poison=(1, 777, bits))
+    got = g.host()
+    bad = np.isnan(got["master"])
+    assert bad.sum() == 1 and bad[777]
+    assert np.isinf(got["m"][777]) and got["v"][777] == np.inf
+    assert np.isnan(got["scales"][777 // 128]) and not got["codes"][768:896].any()
+    assert not np.isnan(np.delete(got["scales"], 777 // 128)).any()
+    g.free()
+
+
 def test_nonfinite_in_clipped_norm():
     log("case +Inf in rank 0 element 17, clipped")
     w = _variant("13B-nd16-clip-int8", quant_block=0)
