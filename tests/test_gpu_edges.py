@@ -107,6 +107,32 @@ def test_ragged_shapes(base, n, nd, qb, clip):
     g.free()
 
 
+@pytest.mark.parametrize("kw,what", [
+    ({"lr": 0.0, "weight_decay": 0.1}, "lr = 0: master unchanged bit for bit, m and v still step"),
+    ({"beta1": 0.0, "beta2": 0.0}, "beta1 = beta2 = 0: m = g, v = g^2"),
+    ({"eps": 1.0, "weight_decay": 0.5, "quant_block": 32}, "large eps and decay, smallest block"),
+])
+def test_degenerate_hyperparameters(kw, what):
+    """Edge values the contract allows, each against the oracle element by
+    element; the first also keeps the master weights bit for bit."""
+    import torch
+
+    log(f"case degenerate hyper-parameters: {what}")
+    w = _variant("tiny-zero1", **kw)
+    n = 10_007
+    g0 = GpuShard(w, n=n)
+    g0.init_state()
+    torch.cuda.synchronize()
+    before = g0.master.cpu().numpy().copy()
+    g0.free()
+    g, _ = _run_pair(w, n, 3)
+    got = g.host()
+    if kw.get("lr") == 0.0:
+        assert np.array_equal(got["master"].view(np.uint32), before.view(np.uint32))
+        assert np.any(got["m"] != 0)
+    g.free()
+
+
 def test_clip_without_spill_and_bias_correction_off():
     log("case clip re-read path, bias correction off")
     w = _variant("13B-nd16-clip-int8", max_norm=0.01)
