@@ -99,9 +99,11 @@ def test_one_graph_serves_every_step(name, n):
     for t in range(1, 7):
         eager.step(t)
         host.copy_(torch.tensor(graphed.shard.consts(w.lr, w.t_of(t)), dtype=torch.float64))
+        # the copy and the replay on one stream: replay() launches on the
+        # current stream, so it is entered here to follow the copy
         with torch.cuda.stream(side):
             consts.copy_(host, non_blocking=True)
-        graph.replay()
+            graph.replay()
         torch.cuda.synchronize()
         a, b = eager.host(), graphed.host()
         for k in a:
@@ -121,7 +123,7 @@ def test_one_graph_serves_every_step(name, n):
         rows = [graphed.shard.consts(w.lr, w.t_of(base + j)) for j in range(3)]
         with torch.cuda.stream(side):
             table.copy_(torch.tensor(rows, dtype=torch.float64).pin_memory(), non_blocking=True)
-        graph3.replay()
+            graph3.replay()
         for j in range(3):
             eager.step(base + j)
         torch.cuda.synchronize()
