@@ -612,6 +612,7 @@ def bench_graph(w, args) -> int:
 
 
 def main() -> int:
+    """Parse the flags, run the chosen measurement, print its JSON line."""
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
