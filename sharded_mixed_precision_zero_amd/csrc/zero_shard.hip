@@ -3,9 +3,12 @@
 //
 // The step is HBM-bound elementwise work, so there is no MFMA here.  Design
 // for CDNA4:
-//  * one lane owns 8 consecutive shard elements: each contribution row is one
-//    128-bit load, each fp32 state array two, the bf16 output one 128-bit
-//    store; a wave64 touches 1 KiB of every row per access, fully coalesced;
+//  * in the reductions one lane owns 8 consecutive shard elements: each
+//    contribution row is one 128-bit load, and a wave64 touches 1 KiB of
+//    every row per access; the one-vector update lays a wave's 512 elements
+//    out so that every access instruction covers one contiguous run (lane l
+//    owns 4 elements at 4l and 4 at 256 + 4l), which keeps the fp32 state
+//    accesses dense;
 //  * the rank-order sum of the bf16 contributions runs in binary64 registers
 //    (binary64 adds issue at the unpacked-binary32 rate on CDNA4, half its
 //    packed peak), exact unless the addends span some 45 binades; the
@@ -76,6 +79,17 @@ constexpr int kNormFronts = ZS_NORM_FRONTS;
 #ifndef ZS_NT_STATE
 #define ZS_NT_STATE 0
 #endif
+#ifndef ZS_DENSE_NT
+#define ZS_DENSE_NT 1
+#endif
+// Nontemporal state loads and stores in the dense one-vector update.
+constexpr bool kDenseNt = ZS_DENSE_NT;
+#ifndef ZS_DENSE_Q_LDS
+#define ZS_DENSE_Q_LDS (48 * 1024)
+#endif
+// LDS reserved (and unused) by each workgroup of the quantizing one-vector
+// update: at most 3 workgroups per CU (160 KiB each).
+constexpr size_t kDenseQLds = ZS_DENSE_Q_LDS;
 #ifndef ZS_NT_SPILL
 #define ZS_NT_SPILL 1
 #endif
@@ -492,6 +506,147 @@ __device__ __forceinline__ void step_vec(const StepArgs<Src> &A, const AdamConst
     if constexpr (QL > 0) quant_lane<QL>(p, nvalid, vec, A.codes, A.scales);
 }
 
+// Dense element layout for one full 512-element chunk c of a wave.  Lane l
+// owns elements 512c + 4l + {0..3} (half 0) and 512c + 256 + 4l + {0..3}
+// (half 1), so that every access instruction of the wave covers one
+// contiguous run: 1 KiB of an fp32 array, 512 B of a bf16 one, 256 B of
+// int8 codes.  (In the per-vector layout a lane owns 8 consecutive elements
+// and each fp32 array takes two 16-byte accesses at a 32-byte lane stride,
+// half of every run per instruction; measured, that pattern loses
+// bandwidth, and with nontemporal accesses loses much more.)  The
+// arithmetic per element is the same, so results are bit-identical.
+__device__ __forceinline__ void add_half(double (&s)[kVec], int h, u32x2 r) {
+  s[4 * h + 0] += static_cast<double>(bf16_lo(r.x));
+  s[4 * h + 1] += static_cast<double>(bf16_hi(r.x));
+  s[4 * h + 2] += static_cast<double>(bf16_lo(r.y));
+  s[4 * h + 3] += static_cast<double>(bf16_hi(r.y));
+}
+
+// a5 on a dense chunk: p[0..3] are elements e0..e0+3, p[4..7] the same 256
+// elements later.  A block of B <= 256 elements is B/4 adjacent lanes of one
+// half, its absmax a lane-shuffle reduction per half; B = 512 is the whole
+// chunk.  Every lane of the wave calls this.
+template <int QL>
+__device__ __forceinline__ void quant_dense(const float (&p)[kVec], int64_t e0, int lane,
+                                            int8_t *codes, float *scales) {
+  constexpr int B = 8 * QL;
+  float a0 = 0.0f, a1 = 0.0f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    a0 = nanmax(a0, __builtin_fabsf(p[e]));
+    a1 = nanmax(a1, __builtin_fabsf(p[e + 4]));
+  }
+  if constexpr (B <= 256) {
+#pragma unroll
+    for (int off = B / 8; off >= 1; off >>= 1) {
+      a0 = nanmax(a0, __shfl_xor(a0, off));
+      a1 = nanmax(a1, __shfl_xor(a1, off));
+    }
+  } else {
+    a0 = nanmax(a0, a1);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) a0 = nanmax(a0, __shfl_xor(a0, off));
+    a1 = a0;
+  }
+  const float s0 = a0 / 127.0f, s1 = a1 / 127.0f;
+  unsigned c0 = 0, c1 = 0;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    c0 |= (unsigned(quant_code(p[e], s0)) & 0xffu) << (8 * e);
+    c1 |= (unsigned(quant_code(p[e + 4], s1)) & 0xffu) << (8 * e);
+  }
+  st<kNtOut>(c0, reinterpret_cast<unsigned *>(codes + e0));
+  st<kNtOut>(c1, reinterpret_cast<unsigned *>(codes + e0 + 256));
+  if constexpr (B <= 256) {
+    if ((lane % (B / 4)) == 0) {
+      scales[e0 / B] = s0;
+      scales[(e0 + 256) / B] = s1;
+    }
+  } else {
+    if (lane == 0) scales[e0 / B] = s0;
+  }
+}
+
+// a1 (bf16 rows) or the spilled gradient, a2 (apply), a3, a4 (+ a5) on the
+// full chunk c in the dense layout.  Every lane of the wave calls it.
+template <int QL>
+__device__ __forceinline__ void step_chunk_dense(const StepArgs<Bf16Rows> &A, const AdamConst &k,
+                                                 int64_t c, int lane, double coef) {
+  constexpr bool nt = kDenseNt;
+  const int64_t e0 = c * 512 + 4 * lane, e1 = e0 + 256;
+  const f32x4 ta = ld<nt>(reinterpret_cast<const f32x4 *>(A.master + e0));
+  const f32x4 tb = ld<nt>(reinterpret_cast<const f32x4 *>(A.master + e1));
+  const f32x4 ma = ld<nt>(reinterpret_cast<const f32x4 *>(A.m + e0));
+  const f32x4 mb = ld<nt>(reinterpret_cast<const f32x4 *>(A.m + e1));
+  const f32x4 va = ld<nt>(reinterpret_cast<const f32x4 *>(A.v + e0));
+  const f32x4 vb = ld<nt>(reinterpret_cast<const f32x4 *>(A.v + e1));
+  float g[kVec];
+  if (A.gbar) {
+    const f32x4 ga = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(A.gbar + e0));
+    const f32x4 gb = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(A.gbar + e1));
+#pragma unroll
+    for (int e = 0; e < 4; ++e) { g[e] = ga[e]; g[e + 4] = gb[e]; }
+  } else {
+    double s[kVec];
+#pragma unroll
+    for (int e = 0; e < kVec; ++e) s[e] = 0.0;
+    for (int k0 = 0; k0 < A.avg.nd; k0 += kRowGroup) {
+      u32x2 r[kRowGroup][2];
+#pragma unroll
+      for (int j = 0; j < kRowGroup; ++j)
+        if (k0 + j < A.avg.nd) {
+          const u32x2 *row = reinterpret_cast<const u32x2 *>(A.src.p[k0 + j]);
+          r[j][0] = __builtin_nontemporal_load(row + e0 / 4);
+          r[j][1] = __builtin_nontemporal_load(row + e1 / 4);
+        }
+#pragma unroll
+      for (int j = 0; j < kRowGroup; ++j)
+        if (k0 + j < A.avg.nd) {
+          add_half(s, 0, r[j][0]);
+          add_half(s, 1, r[j][1]);
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < kVec; ++e) g[e] = average(s[e], A.avg);
+  }
+  float th[kVec], mo[kVec], va8[kVec];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    th[e] = ta[e]; th[e + 4] = tb[e];
+    mo[e] = ma[e]; mo[e + 4] = mb[e];
+    va8[e] = va[e]; va8[e + 4] = vb[e];
+  }
+#pragma unroll
+  for (int e = 0; e < kVec; ++e) adam(coef * static_cast<double>(g[e]), th[e], mo[e], va8[e], k);
+  unsigned pb[4];
+  float p[kVec];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    pb[e] = pack_bf16(th[2 * e], th[2 * e + 1]);
+    p[2 * e] = bf16_lo(pb[e]);
+    p[2 * e + 1] = bf16_hi(pb[e]);
+  }
+  f32x4 o0, o1;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) { o0[e] = th[e]; o1[e] = th[e + 4]; }
+  st<nt>(o0, reinterpret_cast<f32x4 *>(A.master + e0));
+  st<nt>(o1, reinterpret_cast<f32x4 *>(A.master + e1));
+#pragma unroll
+  for (int e = 0; e < 4; ++e) { o0[e] = mo[e]; o1[e] = mo[e + 4]; }
+  st<nt>(o0, reinterpret_cast<f32x4 *>(A.m + e0));
+  st<nt>(o1, reinterpret_cast<f32x4 *>(A.m + e1));
+#pragma unroll
+  for (int e = 0; e < 4; ++e) { o0[e] = va8[e]; o1[e] = va8[e + 4]; }
+  st<nt>(o0, reinterpret_cast<f32x4 *>(A.v + e0));
+  st<nt>(o1, reinterpret_cast<f32x4 *>(A.v + e1));
+  u32x2 q0, q1;
+  q0.x = pb[0]; q0.y = pb[1];
+  q1.x = pb[2]; q1.y = pb[3];
+  st<kNtOut>(q0, reinterpret_cast<u32x2 *>(A.pout + e0));
+  st<kNtOut>(q1, reinterpret_cast<u32x2 *>(A.pout + e1));
+  if constexpr (QL > 0) quant_dense<QL>(p, e0, lane, A.codes, A.scales);
+}
+
 // The fp32 state of one full lane-vector: master, m, v, two 16-byte vectors
 // each.
 struct StateFrag {
@@ -579,11 +734,12 @@ constexpr int kWideMinRows = ZS_WIDE_MIN_ROWS;  // rows from which the update go
 // shard's last, partial chunk goes vector by vector.  The loop condition is
 // uniform across the wave, as the quantizer's shuffles need.
 //
-// The unquantized one-vector form over bf16 rows (the stage-0 and the small
-// unclipped workloads) is compiled for 5 waves per SIMD, which it fits in 94
-// VGPRs (106 and 4 waves otherwise); measured 1.6-1.8% faster on the 13B
-// stage-0 buffer and 3-5% on the GPT-2-sized one.  The other forms would
-// spill at that target and keep the compiler's default.
+// U = 1 over bf16 rows takes every full chunk in the dense layout of
+// step_chunk_dense (nontemporal state accesses); its unquantized form is
+// compiled for 5 waves per SIMD, which it fits in 96 VGPRs, and its
+// quantizing forms run at most 3 workgroups per CU (an LDS reservation made
+// at launch).  The other forms would spill at the 5-wave target and keep the
+// compiler's default.
 template <class Src>
 constexpr bool kBf16Src = false;
 template <>
@@ -604,6 +760,12 @@ __global__ void __launch_bounds__(kThreads)
   constexpr bool nt = ZS_NT_STATE;
   for (int64_t wb = (int64_t(blockIdx.x) * (kThreads / 64) + wave) * span; wb < nvec;
        wb += stride) {
+    if constexpr (U == 1 && kBf16Src<Src>) {
+      if (wb + span <= nfull) {  // a full chunk: the dense layout
+        step_chunk_dense<QL>(A, k, wb / 64, lane, coef);
+        continue;
+      }
+    }
     if (U == 1 || wb + span > nfull) {
 #pragma unroll
       for (int u = 0; u < U; ++u) step_vec<QL, Src>(A, k, wb + 64 * u + lane, coef);
@@ -1174,7 +1336,8 @@ int launch_step(zs_handle *h, const Src &src, const Part &part, const StepTime &
     if (wide)                                                                         \
       hipLaunchKernelGGL((step_kernel<QL, WU, Src>), grid, block, 0, st, A);          \
     else                                                                              \
-      hipLaunchKernelGGL((step_kernel<QL, 1, Src>), grid, block, 0, st, A);           \
+      hipLaunchKernelGGL((step_kernel<QL, 1, Src>), grid, block,                      \
+                         QL > 0 && kBf16Src<Src> ? kDenseQLds : 0, st, A);            \
   } while (0)
   switch (d.quant_block) {
     case 0: ZS_LAUNCH_STEP(0); break;
