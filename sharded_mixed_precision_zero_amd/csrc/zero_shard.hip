@@ -3,12 +3,11 @@
 //
 // The step is HBM-bound elementwise work, so there is no MFMA here.  Design
 // for CDNA4:
-//  * in the reductions one lane owns 8 consecutive shard elements: each
-//    contribution row is one 128-bit load, and a wave64 touches 1 KiB of
-//    every row per access; the one-vector update lays a wave's 512 elements
-//    out so that every access instruction covers one contiguous run (lane l
-//    owns 4 elements at 4l and 4 at 256 + 4l), which keeps the fp32 state
-//    accesses dense;
+//  * the step lays each wave's 512-element chunk out so that every access
+//    instruction covers one contiguous run (lane l owns 4 elements at 4l and
+//    4 at 256 + 4l), which keeps the fp32 state accesses dense; in the norm
+//    pass one lane owns 8 consecutive elements, each contribution row one
+//    128-bit load, a wave64 touching 1 KiB of every row per access;
 //  * the rank-order sum of the bf16 contributions runs in binary64 registers
 //    (binary64 adds issue at the unpacked-binary32 rate on CDNA4, half its
 //    packed peak), exact unless the addends span some 45 binades; the
@@ -82,13 +81,13 @@ constexpr int kNormFronts = ZS_NORM_FRONTS;
 #ifndef ZS_DENSE_NT
 #define ZS_DENSE_NT 1
 #endif
-// Nontemporal state loads and stores in the dense one-vector update.
+// Nontemporal state loads and stores in the step's dense layout.
 constexpr bool kDenseNt = ZS_DENSE_NT;
 #ifndef ZS_DENSE_Q_LDS
 #define ZS_DENSE_Q_LDS (48 * 1024)
 #endif
-// LDS reserved (and unused) by each workgroup of the quantizing one-vector
-// update: at most 3 workgroups per CU (160 KiB each).
+// LDS reserved (and unused) by each workgroup of the quantizing U = 1 step
+// over bf16 rows: at most 3 workgroups per CU (160 KiB each).
 constexpr size_t kDenseQLds = ZS_DENSE_Q_LDS;
 #ifndef ZS_NT_SPILL
 #define ZS_NT_SPILL 1
@@ -515,11 +514,33 @@ __device__ __forceinline__ void step_vec(const StepArgs<Src> &A, const AdamConst
 // half of every run per instruction; measured, that pattern loses
 // bandwidth, and with nontemporal accesses loses much more.)  The
 // arithmetic per element is the same, so results are bit-identical.
-__device__ __forceinline__ void add_half(double (&s)[kVec], int h, u32x2 r) {
-  s[4 * h + 0] += static_cast<double>(bf16_lo(r.x));
-  s[4 * h + 1] += static_cast<double>(bf16_hi(r.x));
-  s[4 * h + 2] += static_cast<double>(bf16_lo(r.y));
-  s[4 * h + 3] += static_cast<double>(bf16_hi(r.y));
+//
+// One row's 4 elements at e of a dense chunk: 8 bytes of bf16, or 4 int8
+// codes and the scale of their block.
+struct Bf16Half {
+  u32x2 r;
+};
+struct Q8Half {
+  unsigned c;
+  float s;
+};
+__device__ __forceinline__ Bf16Half fetch_half(const Bf16Rows &src, int k, int64_t e) {
+  return {__builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(src.p[k]) + e / 4)};
+}
+__device__ __forceinline__ Q8Half fetch_half(const Q8Rows &src, int k, int64_t e) {
+  return {__builtin_nontemporal_load(reinterpret_cast<const unsigned *>(src.c[k]) + e / 4),
+          src.s[k][e >> (src.shift + 3)]};
+}
+__device__ __forceinline__ void accum_half(double (&s)[kVec], int h, const Bf16Half &f) {
+  s[4 * h + 0] += static_cast<double>(bf16_lo(f.r.x));
+  s[4 * h + 1] += static_cast<double>(bf16_hi(f.r.x));
+  s[4 * h + 2] += static_cast<double>(bf16_lo(f.r.y));
+  s[4 * h + 3] += static_cast<double>(bf16_hi(f.r.y));
+}
+__device__ __forceinline__ void accum_half(double (&s)[kVec], int h, const Q8Half &f) {
+  const double sc = static_cast<double>(f.s);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) s[4 * h + e] = add_dequant(s[4 * h + e], f.c, e, sc);
 }
 
 // a5 on a dense chunk: p[0..3] are elements e0..e0+3, p[4..7] the same 256
@@ -567,111 +588,70 @@ __device__ __forceinline__ void quant_dense(const float (&p)[kVec], int64_t e0, 
   }
 }
 
-// a1 (bf16 rows) or the spilled gradient, a2 (apply), a3, a4 (+ a5) on the
-// full chunk c in the dense layout.  Every lane of the wave calls it.
-template <int QL>
-__device__ __forceinline__ void step_chunk_dense(const StepArgs<Bf16Rows> &A, const AdamConst &k,
-                                                 int64_t c, int lane, double coef) {
-  constexpr bool nt = kDenseNt;
-  const int64_t e0 = c * 512 + 4 * lane, e1 = e0 + 256;
-  const f32x4 ta = ld<nt>(reinterpret_cast<const f32x4 *>(A.master + e0));
-  const f32x4 tb = ld<nt>(reinterpret_cast<const f32x4 *>(A.master + e1));
-  const f32x4 ma = ld<nt>(reinterpret_cast<const f32x4 *>(A.m + e0));
-  const f32x4 mb = ld<nt>(reinterpret_cast<const f32x4 *>(A.m + e1));
-  const f32x4 va = ld<nt>(reinterpret_cast<const f32x4 *>(A.v + e0));
-  const f32x4 vb = ld<nt>(reinterpret_cast<const f32x4 *>(A.v + e1));
-  float g[kVec];
-  if (A.gbar) {
-    const f32x4 ga = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(A.gbar + e0));
-    const f32x4 gb = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(A.gbar + e1));
+// a1 on the U full chunks c0, c0+1, ... in the dense layout: the rows are
+// loaded G at a time for all U chunks (2U loads per row in flight) and
+// summed in rank order in binary64, then averaged.
+template <int U, int G, class Src>
+__device__ __forceinline__ void reduce_dense(const Src &src, const Avg &avg, int64_t c0, int lane,
+                                             float (&g)[U][kVec]) {
+  using Half = decltype(fetch_half(src, 0, 0));
+  double s[U][kVec];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) { g[e] = ga[e]; g[e + 4] = gb[e]; }
-  } else {
-    double s[kVec];
+  for (int u = 0; u < U; ++u)
 #pragma unroll
-    for (int e = 0; e < kVec; ++e) s[e] = 0.0;
-    for (int k0 = 0; k0 < A.avg.nd; k0 += kRowGroup) {
-      u32x2 r[kRowGroup][2];
+    for (int e = 0; e < kVec; ++e) s[u][e] = 0.0;
+  for (int k0 = 0; k0 < avg.nd; k0 += G) {
+    Half r[U][G][2];
 #pragma unroll
-      for (int j = 0; j < kRowGroup; ++j)
-        if (k0 + j < A.avg.nd) {
-          const u32x2 *row = reinterpret_cast<const u32x2 *>(A.src.p[k0 + j]);
-          r[j][0] = __builtin_nontemporal_load(row + e0 / 4);
-          r[j][1] = __builtin_nontemporal_load(row + e1 / 4);
+    for (int j = 0; j < G; ++j)
+      if (k0 + j < avg.nd)
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int64_t e0 = (c0 + u) * 512 + 4 * lane;
+          r[u][j][0] = fetch_half(src, k0 + j, e0);
+          r[u][j][1] = fetch_half(src, k0 + j, e0 + 256);
         }
 #pragma unroll
-      for (int j = 0; j < kRowGroup; ++j)
-        if (k0 + j < A.avg.nd) {
-          add_half(s, 0, r[j][0]);
-          add_half(s, 1, r[j][1]);
+    for (int j = 0; j < G; ++j)
+      if (k0 + j < avg.nd)
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          accum_half(s[u], 0, r[u][j][0]);
+          accum_half(s[u], 1, r[u][j][1]);
         }
-    }
-#pragma unroll
-    for (int e = 0; e < kVec; ++e) g[e] = average(s[e], A.avg);
-  }
-  float th[kVec], mo[kVec], va8[kVec];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    th[e] = ta[e]; th[e + 4] = tb[e];
-    mo[e] = ma[e]; mo[e + 4] = mb[e];
-    va8[e] = va[e]; va8[e + 4] = vb[e];
   }
 #pragma unroll
-  for (int e = 0; e < kVec; ++e) adam(coef * static_cast<double>(g[e]), th[e], mo[e], va8[e], k);
-  unsigned pb[4];
-  float p[kVec];
+  for (int u = 0; u < U; ++u)
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    pb[e] = pack_bf16(th[2 * e], th[2 * e + 1]);
-    p[2 * e] = bf16_lo(pb[e]);
-    p[2 * e + 1] = bf16_hi(pb[e]);
-  }
-  f32x4 o0, o1;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) { o0[e] = th[e]; o1[e] = th[e + 4]; }
-  st<nt>(o0, reinterpret_cast<f32x4 *>(A.master + e0));
-  st<nt>(o1, reinterpret_cast<f32x4 *>(A.master + e1));
-#pragma unroll
-  for (int e = 0; e < 4; ++e) { o0[e] = mo[e]; o1[e] = mo[e + 4]; }
-  st<nt>(o0, reinterpret_cast<f32x4 *>(A.m + e0));
-  st<nt>(o1, reinterpret_cast<f32x4 *>(A.m + e1));
-#pragma unroll
-  for (int e = 0; e < 4; ++e) { o0[e] = va8[e]; o1[e] = va8[e + 4]; }
-  st<nt>(o0, reinterpret_cast<f32x4 *>(A.v + e0));
-  st<nt>(o1, reinterpret_cast<f32x4 *>(A.v + e1));
-  u32x2 q0, q1;
-  q0.x = pb[0]; q0.y = pb[1];
-  q1.x = pb[2]; q1.y = pb[3];
-  st<kNtOut>(q0, reinterpret_cast<u32x2 *>(A.pout + e0));
-  st<kNtOut>(q1, reinterpret_cast<u32x2 *>(A.pout + e1));
-  if constexpr (QL > 0) quant_dense<QL>(p, e0, lane, A.codes, A.scales);
+    for (int e = 0; e < kVec; ++e) g[u][e] = average(s[u][e], avg);
 }
 
-// The fp32 state of one full lane-vector: master, m, v, two 16-byte vectors
-// each.
-struct StateFrag {
+// The fp32 state of a lane's 8 elements of a dense chunk (e0 = its first):
+// master, m and v, one 16-byte vector per half each, nontemporal.
+struct DenseState {
   f32x4 t[2], m[2], v[2];
 };
 
-template <bool NT, class Src>
-__device__ __forceinline__ void load_state(const StepArgs<Src> &A, int64_t vec, StateFrag &s) {
-  const f32x4 *t4 = reinterpret_cast<const f32x4 *>(A.master) + 2 * vec;
-  const f32x4 *m4 = reinterpret_cast<const f32x4 *>(A.m) + 2 * vec;
-  const f32x4 *v4 = reinterpret_cast<const f32x4 *>(A.v) + 2 * vec;
-  s.t[0] = ld<NT>(t4); s.t[1] = ld<NT>(t4 + 1);
-  s.m[0] = ld<NT>(m4); s.m[1] = ld<NT>(m4 + 1);
-  s.v[0] = ld<NT>(v4); s.v[1] = ld<NT>(v4 + 1);
+template <class Src>
+__device__ __forceinline__ void load_dense(const StepArgs<Src> &A, int64_t e0, DenseState &s) {
+  constexpr bool nt = kDenseNt;
+  const f32x4 *t4 = reinterpret_cast<const f32x4 *>(A.master + e0);
+  const f32x4 *m4 = reinterpret_cast<const f32x4 *>(A.m + e0);
+  const f32x4 *v4 = reinterpret_cast<const f32x4 *>(A.v + e0);
+  s.t[0] = ld<nt>(t4); s.t[1] = ld<nt>(t4 + 64);
+  s.m[0] = ld<nt>(m4); s.m[1] = ld<nt>(m4 + 64);
+  s.v[0] = ld<nt>(v4); s.v[1] = ld<nt>(v4 + 64);
 }
 
-// a2 (apply) + a3 + a4 (+ a5) on one full lane-vector whose averaged
-// gradient is g and whose state was loaded into s; every lane of the wave
-// calls it together when QL > 0.
+// a2 (apply) + a3 + a4 (+ a5) on a lane's 8 elements of a dense chunk,
+// given their averaged gradient g and state s.  Every lane of the wave
+// calls it together (the quantizer's shuffles).
 template <int QL, class Src>
-__device__ __forceinline__ void update_full(const StepArgs<Src> &A, const AdamConst &k,
-                                            int64_t vec, double coef, const float (&g)[kVec],
-                                            const StateFrag &s) {
-  constexpr bool nt = ZS_NT_STATE;
-  float th[kVec], mo[kVec], va[kVec], p[kVec];
+__device__ __forceinline__ void update_dense(const StepArgs<Src> &A, const AdamConst &k,
+                                             int64_t e0, int lane, double coef,
+                                             const float (&g)[kVec], const DenseState &s) {
+  constexpr bool nt = kDenseNt;
+  float th[kVec], mo[kVec], va[kVec];
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     th[e] = s.t[0][e]; th[e + 4] = s.t[1][e];
@@ -681,29 +661,53 @@ __device__ __forceinline__ void update_full(const StepArgs<Src> &A, const AdamCo
 #pragma unroll
   for (int e = 0; e < kVec; ++e) adam(coef * static_cast<double>(g[e]), th[e], mo[e], va[e], k);
   unsigned pb[4];
+  float p[kVec];
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     pb[e] = pack_bf16(th[2 * e], th[2 * e + 1]);
     p[2 * e] = bf16_lo(pb[e]);
     p[2 * e + 1] = bf16_hi(pb[e]);
   }
-  f32x4 o[6];
+  f32x4 o0, o1;
+  f32x4 *t4 = reinterpret_cast<f32x4 *>(A.master + e0);
+  f32x4 *m4 = reinterpret_cast<f32x4 *>(A.m + e0);
+  f32x4 *v4 = reinterpret_cast<f32x4 *>(A.v + e0);
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    o[0][e] = th[e]; o[1][e] = th[e + 4];
-    o[2][e] = mo[e]; o[3][e] = mo[e + 4];
-    o[4][e] = va[e]; o[5][e] = va[e + 4];
+  for (int e = 0; e < 4; ++e) { o0[e] = th[e]; o1[e] = th[e + 4]; }
+  st<nt>(o0, t4); st<nt>(o1, t4 + 64);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) { o0[e] = mo[e]; o1[e] = mo[e + 4]; }
+  st<nt>(o0, m4); st<nt>(o1, m4 + 64);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) { o0[e] = va[e]; o1[e] = va[e + 4]; }
+  st<nt>(o0, v4); st<nt>(o1, v4 + 64);
+  u32x2 q0, q1;
+  q0.x = pb[0]; q0.y = pb[1];
+  q1.x = pb[2]; q1.y = pb[3];
+  st<kNtOut>(q0, reinterpret_cast<u32x2 *>(A.pout + e0));
+  st<kNtOut>(q1, reinterpret_cast<u32x2 *>(A.pout + e0 + 256));
+  if constexpr (QL > 0) quant_dense<QL>(p, e0, lane, A.codes, A.scales);
+}
+
+// a1 (rows) or the spilled gradient, then the update, on the full chunk c in
+// the dense layout, one chunk per wave.
+template <int QL, class Src>
+__device__ __forceinline__ void step_chunk_dense(const StepArgs<Src> &A, const AdamConst &k,
+                                                 int64_t c, int lane, double coef) {
+  const int64_t e0 = c * 512 + 4 * lane;
+  float g[1][kVec];
+  if (A.gbar) {
+    const f32x4 *g4 = reinterpret_cast<const f32x4 *>(A.gbar + e0);
+    const f32x4 ga = __builtin_nontemporal_load(g4);
+    const f32x4 gb = __builtin_nontemporal_load(g4 + 64);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) { g[0][e] = ga[e]; g[0][e + 4] = gb[e]; }
+  } else {
+    reduce_dense<1, kRowGroup>(A.src, A.avg, c, lane, g);
   }
-  f32x4 *t4 = reinterpret_cast<f32x4 *>(A.master) + 2 * vec;
-  f32x4 *m4 = reinterpret_cast<f32x4 *>(A.m) + 2 * vec;
-  f32x4 *v4 = reinterpret_cast<f32x4 *>(A.v) + 2 * vec;
-  st<nt>(o[0], t4); st<nt>(o[1], t4 + 1);
-  st<nt>(o[2], m4); st<nt>(o[3], m4 + 1);
-  st<nt>(o[4], v4); st<nt>(o[5], v4 + 1);
-  u32x4 pv;
-  pv.x = pb[0]; pv.y = pb[1]; pv.z = pb[2]; pv.w = pb[3];
-  st<kNtOut>(pv, reinterpret_cast<u32x4 *>(A.pout) + vec);
-  if constexpr (QL > 0) quant_lane<QL>(p, kVec, vec, A.codes, A.scales);
+  DenseState s;
+  load_dense(A, e0, s);
+  update_dense<QL>(A, k, e0, lane, coef, g[0], s);
 }
 
 // The step's constants: fixed at the call, or read from the caller's device
@@ -725,21 +729,21 @@ __device__ __forceinline__ AdamConst step_consts(const StepArgs<Src> &A) {
 #endif
 constexpr int kWideMinRows = ZS_WIDE_MIN_ROWS;  // rows from which the update goes wide
 
-// a1 + a2 (apply) + a3 + a4 (+ a5 when QL > 0).  Each wave owns a chunk of
-// 64*U consecutive lane-vectors per iteration (lane l takes v0+l, v0+64+l,
-// ...).  U = 1: one vector per lane, state, gradient and outputs together.
-// U > 1 (many contribution rows): the rows of all U vectors are reduced
-// first, so that every wave reads U KiB runs of each row with U*G 16-byte
-// loads in flight, then each vector's state is updated in turn.  The
-// shard's last, partial chunk goes vector by vector.  The loop condition is
-// uniform across the wave, as the quantizer's shuffles need.
+// a1 + a2 (apply) + a3 + a4 (+ a5 when QL > 0).  Each wave owns U
+// consecutive 512-element chunks per iteration, in the dense layout.  U = 1:
+// one chunk, state, gradient and outputs together.  U > 1 (many
+// contribution rows): the rows of all U chunks are reduced first, so that
+// every wave reads U runs of 512 B (bf16) of each row with 2*U*G loads in
+// flight, then each chunk's state is updated in turn.  The shard's last,
+// partial chunk goes vector by vector (lane l takes lane-vectors wb + l,
+// wb + 64 + l, ...).  The loop condition is uniform across the wave, as the
+// quantizer's shuffles need.
 //
-// U = 1 over bf16 rows takes every full chunk in the dense layout of
-// step_chunk_dense (nontemporal state accesses); its unquantized form is
-// compiled for 5 waves per SIMD, which it fits in 96 VGPRs, and its
-// quantizing forms run at most 3 workgroups per CU (an LDS reservation made
-// at launch).  The other forms would spill at the 5-wave target and keep the
-// compiler's default.
+// The unquantized U = 1 form over bf16 rows is compiled for 5 waves per
+// SIMD, which it fits in 96 VGPRs, and the quantizing U = 1 forms over bf16
+// rows run at most 3 workgroups per CU (an LDS reservation made at launch).
+// The other forms would spill at the 5-wave target and keep the compiler's
+// default.
 template <class Src>
 constexpr bool kBf16Src = false;
 template <>
@@ -757,28 +761,25 @@ __global__ void __launch_bounds__(kThreads)
   const int64_t stride = int64_t(gridDim.x) * (kThreads / 64) * span;
   const double coef = A.sumsq ? clip_coef(*A.sumsq, A.max_norm) : 1.0;
   const AdamConst k = step_consts(A);
-  constexpr bool nt = ZS_NT_STATE;
   for (int64_t wb = (int64_t(blockIdx.x) * (kThreads / 64) + wave) * span; wb < nvec;
        wb += stride) {
-    if constexpr (U == 1 && kBf16Src<Src>) {
-      if (wb + span <= nfull) {  // a full chunk: the dense layout
-        step_chunk_dense<QL>(A, k, wb / 64, lane, coef);
-        continue;
-      }
-    }
-    if (U == 1 || wb + span > nfull) {
+    if (wb + span > nfull) {
 #pragma unroll
       for (int u = 0; u < U; ++u) step_vec<QL, Src>(A, k, wb + 64 * u + lane, coef);
       continue;
     }
-    float g[U][kVec];
-    reduce_average_wave<U, Tune<Src>::wide_group>(A.src, A.avg, wb + lane, g);
+    if constexpr (U == 1) {
+      step_chunk_dense<QL>(A, k, wb / 64, lane, coef);
+    } else {
+      float g[U][kVec];
+      reduce_dense<U, Tune<Src>::wide_group>(A.src, A.avg, wb / 64, lane, g);
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t vec = wb + 64 * u + lane;
-      StateFrag sf;
-      load_state<nt>(A, vec, sf);
-      update_full<QL>(A, k, vec, coef, g[u], sf);
+      for (int u = 0; u < U; ++u) {
+        const int64_t e0 = (wb / 64 + u) * 512 + 4 * lane;
+        DenseState s;
+        load_dense(A, e0, s);
+        update_dense<QL>(A, k, e0, lane, coef, g[u], s);
+      }
     }
   }
 }
