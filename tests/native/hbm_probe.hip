@@ -31,6 +31,7 @@
 // per mix.
 // Build:  hipcc --offload-arch=gfx950 -O3 hbm_probe.hip -o hbm_probe
 // Run:    hbm_probe [mix ...]   (default: every mix)
+//         hbm_probe alu         (the ALU-carrying sweep of the update mixes)
 #include <hip/hip_runtime.h>
 
 #include <cstdio>
@@ -219,6 +220,101 @@ static void mix(const char *name, const Pools &P, const std::vector<std::string>
   std::fflush(stdout);
 }
 
+// ALU-carrying form of the probe (run with the argument `alu`): one-shot,
+// one lane-vector per lane; after its R loads each lane runs K binary64
+// fused multiply-adds in 8 independent chains (the 8 elements of a lane in
+// the update) seeded from the loaded data, and folds their (always false)
+// overflow test into what it stores, so the W stores wait for the
+// arithmetic as the update's do.  K is swept from 0 to about the update's
+// own VALU work per lane-vector.
+template <int R, int W, bool LNT, bool SNT, int K>
+__global__ void __launch_bounds__(256) probe_alu(const Streams S, long n, unsigned *sink) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const long wb = (long(blockIdx.x) * 4 + wave) * 64;
+  if (wb + 64 > n) return;
+  u32x4 v = (u32x4){0, 0, 0, 0};
+#pragma unroll
+  for (int r = 0; r < R; ++r) v += load<LNT>(S.in[r] + wb + lane);
+  double x[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) x[e] = double((v[e & 3] >> (8 * (e >> 2))) & 0xff) * 1e-3;
+  for (int i = 0; i < K / 8; ++i)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = __builtin_fma(x[e], 0.999999, 1e-9);
+  unsigned f = 0;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) f |= x[e] > 1e300 ? 1u : 0u;
+#pragma unroll
+  for (int w = 0; w < W; ++w) store<SNT>(v + (unsigned)w + f, S.out[w] + wb + lane);
+  if (f == 0x9e3779b9u) sink[0] = f;
+}
+
+template <int R, int W, bool LNT, bool SNT, int K>
+static double run_alu(const Pools &P, long n, int cap) {
+  Streams S;
+  std::memset(&S, 0, sizeof S);
+  const long stream_bytes = n * 16 + kGap[0];
+  const long base = 2L << 20;
+  for (int i = 0; i < R; ++i) S.in[i] = reinterpret_cast<const u32x4 *>(P.in + base + i * stream_bytes);
+  for (int i = 0; i < W; ++i) S.out[i] = reinterpret_cast<u32x4 *>(P.out + base + i * stream_bytes);
+  if (size_t(base + R * stream_bytes) > P.in_bytes || size_t(base + W * stream_bytes) > P.out_bytes)
+    return -1;
+  const size_t lds_of[5] = {0, 96 * 1024, 64 * 1024, 48 * 1024, 40 * 1024};
+  const size_t lds = lds_of[cap];
+  auto k = probe_alu<R, W, LNT, SNT, K>;
+  if (lds > 64 * 1024 &&
+      hipFuncSetAttribute(reinterpret_cast<const void *>(k),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, int(lds)) != hipSuccess) {
+    (void)hipGetLastError();
+    return -1;
+  }
+  const long grid = n / 256;
+  hipEvent_t a, b;
+  check(hipEventCreate(&a), "event");
+  check(hipEventCreate(&b), "event");
+  hipLaunchKernelGGL(k, dim3(unsigned(grid)), dim3(256), lds, 0, S, n, P.sink);
+  if (hipGetLastError() != hipSuccess) {
+    check(hipEventDestroy(a), "event");
+    check(hipEventDestroy(b), "event");
+    return -1;
+  }
+  check(hipEventRecord(a), "record");
+  const int iters = 3;
+  for (int it = 0; it < iters; ++it)
+    hipLaunchKernelGGL(k, dim3(unsigned(grid)), dim3(256), lds, 0, S, n, P.sink);
+  check(hipGetLastError(), "launch");
+  check(hipEventRecord(b), "record");
+  check(hipEventSynchronize(b), "sync");
+  float ms = 0;
+  check(hipEventElapsedTime(&ms, a, b), "elapsed");
+  check(hipEventDestroy(a), "event");
+  check(hipEventDestroy(b), "event");
+  return double(R + W) * n * 16.0 * iters / (ms * 1e-3) / 1e9;
+}
+
+template <int R, int W, int K>
+static void alu_shapes(const char *mix, const Pools &P, long n) {
+  const struct { int cap; const char *name; } caps[] = {{0, "oneshot"}, {2, "oneshot-cap2"},
+                                                        {3, "oneshot-cap3"}};
+  for (const auto &c : caps) {
+    const double pl = run_alu<R, W, false, false, K>(P, n, c.cap);
+    const double nt = run_alu<R, W, true, true, K>(P, n, c.cap);
+    std::printf("ALU %-7s K=%-4d %-13s Lpl-Spl %7.0f GB/s  Lnt-Snt %7.0f GB/s\n", mix, K, c.name,
+                pl, nt);
+  }
+  std::fflush(stdout);
+}
+
+template <int R, int W>
+static void alu_mix(const char *mix, const Pools &P) {
+  const long unit = (2L << 20) / 16;
+  long n = long(6e9) / (long(R + W) * 16) / unit * unit;
+  alu_shapes<R, W, 0>(mix, P, n);
+  alu_shapes<R, W, 256>(mix, P, n);
+  alu_shapes<R, W, 512>(mix, P, n);
+  alu_shapes<R, W, 768>(mix, P, n);
+}
+
 int main(int argc, char **argv) {
   std::vector<std::string> want;
   for (int i = 1; i < argc; ++i) want.emplace_back(argv[i]);
@@ -238,6 +334,14 @@ int main(int argc, char **argv) {
               "per launch / mean of 3 launches\n",
               prop.gcnArchName, P.cus, size_t(prop.sharedMemPerBlock),
               size_t(prop.maxSharedMemoryPerMultiProcessor));
+  if (!want.empty() && want[0] == "alu") {  // the ALU-carrying sweep only
+    alu_mix<8, 7>("upd", P);
+    alu_mix<7, 7>("nd1", P);
+    check(hipFree(P.in), "free");
+    check(hipFree(P.out), "free");
+    check(hipFree(P.sink), "free");
+    return 0;
+  }
   mix<1, 0>("read", P, want);
   mix<0, 1>("write", P, want);
   mix<1, 1>("copy", P, want);
