@@ -25,35 +25,43 @@
 //   nd1    R7  W7   N_d = 1 update: one bf16 row + state in, state + bf16 out
 //   nd64   R70 W7   N_d = 64 update: 64 bf16 rows + state in, state + bf16 out
 //   q8nd64 R38 W7   N_d = 64 int8 rows (8 B per lane-vector) + state in
-// Every access is in bounds: a stream holds n vectors, n a multiple of every
-// sweep span times 8, one-shot grids cover exactly n, persistent loops stop
-// at the last whole span.  Prints one line per configuration and the best
-// per mix.
+// The exact-shape mixes (names ending in -x) instead reproduce each kernel's
+// streams one for one: an array of z bytes per shard element is one stream
+// (an fp32 array is one stream, not two), the state is read and written
+// back in place, and every access has the kernel's lane layout (see
+// probe_x below).
+// Every access is in bounds: a stream holds n vectors (exact shapes: n
+// elements, n a multiple of 2^20), n a multiple of every sweep span times 8,
+// one-shot grids cover exactly n, persistent loops stop at the last whole
+// span.  Prints one line per configuration and the best per mix.
 // Build:  hipcc --offload-arch=gfx950 -O3 hbm_probe.hip -o hbm_probe
 // Run:    hbm_probe [mix ...]   (default: every mix)
 //         hbm_probe alu         (the ALU-carrying sweep of the update mixes)
+//         hbm_probe norm16-x upd-x  (any subset of mixes, by name)
 #include <hip/hip_runtime.h>
 
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
 #include <string>
+#include <type_traits>
 #include <vector>
 
 using u32x4 = unsigned int __attribute__((ext_vector_type(4)));
+using u32x2 = unsigned int __attribute__((ext_vector_type(2)));
 constexpr int kMaxIn = 70, kMaxOut = 7;
 struct Streams {
   const u32x4 *in[kMaxIn];
   u32x4 *out[kMaxOut];
 };
 
-template <bool NT>
-__device__ __forceinline__ u32x4 load(const u32x4 *p) {
+template <bool NT, class T>
+__device__ __forceinline__ T load(const T *p) {
   if constexpr (NT) return __builtin_nontemporal_load(p);
   else return *p;
 }
-template <bool NT>
-__device__ __forceinline__ void store(u32x4 v, u32x4 *p) {
+template <bool NT, class T>
+__device__ __forceinline__ void store(T v, T *p) {
   if constexpr (NT) __builtin_nontemporal_store(v, p);
   else *p = v;
 }
@@ -315,6 +323,253 @@ static void alu_mix(const char *mix, const Pools &P) {
   alu_shapes<R, W, 768>(mix, P, n);
 }
 
+// ---------------------------------------------------------------- exact shapes
+// probe_x streams, per 512-element chunk of the shard, NB1 read streams of 1
+// byte per element (int8 rows), NB2 of 2 (bf16 rows), NF4 of 4 (the spill),
+// NS4 streams of 4 read and then rewritten in place (fp32 master, m, v), and
+// NO1 / NO2 / NO4 write streams of 1 / 2 / 4 bytes (int8 codes, bf16, the
+// spill).  Lane layouts, as the kernels use them:
+//   DENSE (the step): lane l touches elements 4l..4l+3 and 256+4l..256+4l+3
+//     of the chunk, two accesses of 4z bytes per stream;
+//   per-vector (the norm pass): lane l touches elements 8l..8l+7, one
+//     access of 8z bytes (two 16-byte ones for z = 4).
+// Each wave sweeps U consecutive chunks: all loads of the U chunks, then all
+// stores, as the kernels order them.
+constexpr int kMaxB = 64;
+struct XStreams {
+  const char *b1[kMaxB];
+  const char *b2[kMaxB];
+  const char *f4[1];
+  char *s4[3];
+  char *o1[1], *o2[1], *o4[1];
+};
+
+__device__ __forceinline__ void fold(u32x4 &a, unsigned w) { a.x += w; }
+__device__ __forceinline__ void fold(u32x4 &a, u32x2 w) { a.x += w.x; a.y += w.y; }
+__device__ __forceinline__ void fold(u32x4 &a, u32x4 w) { a += w; }
+__device__ __forceinline__ void as_word(const u32x4 &a, unsigned &w) { w = a.x; }
+__device__ __forceinline__ void as_word(const u32x4 &a, u32x2 &w) { w = (u32x2){a.x, a.y}; }
+__device__ __forceinline__ void as_word(const u32x4 &a, u32x4 &w) { w = a; }
+
+// A lane's accesses to a stream of z bytes per element in chunk c: the word
+// type T and the word indexes (count k).
+template <int Z, bool DENSE>
+struct XAcc;
+template <int Z>
+struct XAcc<Z, true> {  // two words of 4z bytes: elements 4l and 256 + 4l
+  using T = typename std::conditional<Z == 1, unsigned,
+                                      typename std::conditional<Z == 2, u32x2, u32x4>::type>::type;
+  static constexpr int k = 2;
+  __device__ static void words(long c, int lane, long (&w)[2]) {
+    w[0] = (c * 512 + 4 * lane) / 4;
+    w[1] = (c * 512 + 256 + 4 * lane) / 4;
+  }
+};
+template <>
+struct XAcc<4, false> {  // 8 elements at 8l: two adjacent 16-byte words
+  using T = u32x4;
+  static constexpr int k = 2;
+  __device__ static void words(long c, int lane, long (&w)[2]) {
+    w[0] = (c * 512 + 8 * lane) / 4;
+    w[1] = w[0] + 1;
+  }
+};
+template <>
+struct XAcc<2, false> {  // 8 elements at 8l: one 16-byte word
+  using T = u32x4;
+  static constexpr int k = 1;
+  __device__ static void words(long c, int lane, long (&w)[2]) { w[0] = (c * 512 + 8 * lane) / 8; }
+};
+template <>
+struct XAcc<1, false> {  // 8 elements at 8l: one 8-byte word
+  using T = u32x2;
+  static constexpr int k = 1;
+  __device__ static void words(long c, int lane, long (&w)[2]) { w[0] = (c * 512 + 8 * lane) / 8; }
+};
+
+template <int Z, bool DENSE, bool NT>
+__device__ __forceinline__ void x_read(const char *p, long c, int lane, u32x4 &acc) {
+  using A = XAcc<Z, DENSE>;
+  long w[2];
+  A::words(c, lane, w);
+  const typename A::T *q = reinterpret_cast<const typename A::T *>(p);
+#pragma unroll
+  for (int i = 0; i < A::k; ++i) fold(acc, load<NT>(q + w[i]));
+}
+
+template <int Z, bool DENSE, bool NT>
+__device__ __forceinline__ void x_write(char *p, long c, int lane, const u32x4 &v) {
+  using A = XAcc<Z, DENSE>;
+  long w[2];
+  A::words(c, lane, w);
+  typename A::T *q = reinterpret_cast<typename A::T *>(p);
+  typename A::T x;
+  as_word(v, x);
+#pragma unroll
+  for (int i = 0; i < A::k; ++i) store<NT>(x, q + w[i]);
+}
+
+template <int NB1, int NB2, int NF4, int NS4, int NO1, int NO2, int NO4, bool DENSE, int U,
+          bool LNT, bool SNT>
+__global__ void __launch_bounds__(256) probe_x(const XStreams S, long nchunks, int mode,
+                                               unsigned *sink) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const long grid = gridDim.x;
+  long blk = blockIdx.x;
+  if (mode == 1) blk = (blk % 8) * (grid / 8) + blk / 8;
+  const long first = (blk * 4 + wave) * U;
+  const long stride = mode == 2 ? grid * 4 * U : nchunks;
+  unsigned acc_all = 0;
+  for (long c0 = first; c0 + U <= nchunks; c0 += stride) {
+    u32x4 a[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      a[u] = (u32x4){0, 0, 0, 0};
+#pragma unroll
+      for (int i = 0; i < NB1; ++i) x_read<1, DENSE, LNT>(S.b1[i], c0 + u, lane, a[u]);
+#pragma unroll
+      for (int i = 0; i < NB2; ++i) x_read<2, DENSE, LNT>(S.b2[i], c0 + u, lane, a[u]);
+#pragma unroll
+      for (int i = 0; i < NF4; ++i) x_read<4, DENSE, LNT>(S.f4[i], c0 + u, lane, a[u]);
+#pragma unroll
+      for (int i = 0; i < NS4; ++i) x_read<4, DENSE, LNT>(S.s4[i], c0 + u, lane, a[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+#pragma unroll
+      for (int i = 0; i < NS4; ++i) x_write<4, DENSE, SNT>(S.s4[i], c0 + u, lane, a[u] + 1u);
+#pragma unroll
+      for (int i = 0; i < NO1; ++i) x_write<1, DENSE, SNT>(S.o1[i], c0 + u, lane, a[u]);
+#pragma unroll
+      for (int i = 0; i < NO2; ++i) x_write<2, DENSE, SNT>(S.o2[i], c0 + u, lane, a[u]);
+#pragma unroll
+      for (int i = 0; i < NO4; ++i) x_write<4, DENSE, SNT>(S.o4[i], c0 + u, lane, a[u]);
+      acc_all += a[u].x ^ a[u].w;
+    }
+  }
+  if (acc_all == 0x9e3779b9u) sink[0] = acc_all;
+}
+
+template <int NB1, int NB2, int NF4, int NS4, int NO1, int NO2, int NO4>
+constexpr long x_bytes_per_elem() {
+  return NB1 + 2L * NB2 + 4L * NF4 + 8L * NS4 + NO1 + 2L * NO2 + 4L * NO4;
+}
+
+template <int NB1, int NB2, int NF4, int NS4, int NO1, int NO2, int NO4, bool DENSE, int U,
+          bool LNT, bool SNT>
+static double run_x(const Pools &P, long n, int mode, int per_cu, int cap) {
+  XStreams S;
+  std::memset(&S, 0, sizeof S);
+  const long gap = 1280, base = 2L << 20;
+  long in_off = base, out_off = base;
+  auto take_in = [&](long z) -> char * {
+    char *p = P.in + in_off;
+    in_off += n * z + gap;
+    return p;
+  };
+  auto take_out = [&](long z) -> char * {
+    char *p = P.out + out_off;
+    out_off += n * z + gap;
+    return p;
+  };
+  for (int i = 0; i < NB1; ++i) S.b1[i] = take_in(1);
+  for (int i = 0; i < NB2; ++i) S.b2[i] = take_in(2);
+  for (int i = 0; i < NF4; ++i) S.f4[i] = take_in(4);
+  for (int i = 0; i < NS4; ++i) S.s4[i] = take_in(4);
+  for (int i = 0; i < NO1; ++i) S.o1[i] = take_out(1);
+  for (int i = 0; i < NO2; ++i) S.o2[i] = take_out(2);
+  for (int i = 0; i < NO4; ++i) S.o4[i] = take_out(4);
+  if (size_t(in_off) > P.in_bytes || size_t(out_off) > P.out_bytes) return -1;
+  const long nchunks = n / 512;
+  long grid = mode == 2 ? long(P.cus) * per_cu : nchunks / (4L * U);
+  if (mode != 2 && (nchunks % (4L * U) != 0 || grid % 8 != 0)) return -1;
+  const size_t lds_of[5] = {0, 96 * 1024, 64 * 1024, 48 * 1024, 40 * 1024};
+  const size_t lds = lds_of[cap];
+  auto k = probe_x<NB1, NB2, NF4, NS4, NO1, NO2, NO4, DENSE, U, LNT, SNT>;
+  if (lds > 64 * 1024 &&
+      hipFuncSetAttribute(reinterpret_cast<const void *>(k),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, int(lds)) != hipSuccess) {
+    (void)hipGetLastError();
+    return -1;
+  }
+  hipEvent_t a, b;
+  check(hipEventCreate(&a), "event");
+  check(hipEventCreate(&b), "event");
+  hipLaunchKernelGGL(k, dim3(unsigned(grid)), dim3(256), lds, 0, S, nchunks, mode, P.sink);
+  if (hipGetLastError() != hipSuccess) {
+    check(hipEventDestroy(a), "event");
+    check(hipEventDestroy(b), "event");
+    return -1;
+  }
+  check(hipEventRecord(a), "record");
+  const int iters = 3;
+  for (int it = 0; it < iters; ++it)
+    hipLaunchKernelGGL(k, dim3(unsigned(grid)), dim3(256), lds, 0, S, nchunks, mode, P.sink);
+  check(hipGetLastError(), "launch");
+  check(hipEventRecord(b), "record");
+  check(hipEventSynchronize(b), "sync");
+  float ms = 0;
+  check(hipEventElapsedTime(&ms, a, b), "elapsed");
+  check(hipEventDestroy(a), "event");
+  check(hipEventDestroy(b), "event");
+  const double bytes = double(x_bytes_per_elem<NB1, NB2, NF4, NS4, NO1, NO2, NO4>()) * n;
+  return bytes * iters / (ms * 1e-3) / 1e9;
+}
+
+template <int NB1, int NB2, int NF4, int NS4, int NO1, int NO2, int NO4, bool DENSE, int U,
+          bool LNT, bool SNT>
+static void shapes_x(const char *mix, const Pools &P, long n, Best &best) {
+  const char *pol = LNT ? (SNT ? "Lnt-Snt" : "Lnt-Spl") : (SNT ? "Lpl-Snt" : "Lpl-Spl");
+  struct Shape { int mode, per_cu, cap; const char *name; };
+  const Shape sh[] = {{0, 0, 0, "oneshot"},      {1, 0, 0, "oneshot-xcd"},
+                      {0, 0, 1, "oneshot-cap1"}, {1, 0, 1, "oneshot-xcd-cap1"},
+                      {0, 0, 2, "oneshot-cap2"}, {1, 0, 2, "oneshot-xcd-cap2"},
+                      {0, 0, 3, "oneshot-cap3"}, {1, 0, 3, "oneshot-xcd-cap3"},
+                      {0, 0, 4, "oneshot-cap4"}, {1, 0, 4, "oneshot-xcd-cap4"},
+                      {2, 8, 0, "persist8"}};
+  for (const Shape &s : sh) {
+    const double g =
+        run_x<NB1, NB2, NF4, NS4, NO1, NO2, NO4, DENSE, U, LNT, SNT>(P, n, s.mode, s.per_cu, s.cap);
+    if (g < 0) continue;
+    std::printf("%-9s %s U%d %-17s %7.0f GB/s\n", mix, pol, U, s.name, g);
+    if (g > best.gbs) {
+      best.gbs = g;
+      std::snprintf(best.what, sizeof best.what, "%s U%d %s", pol, U, s.name);
+    }
+  }
+  std::fflush(stdout);
+}
+
+template <int NB1, int NB2, int NF4, int NS4, int NO1, int NO2, int NO4, bool DENSE, int U>
+static void policies_x(const char *mix, const Pools &P, long n, Best &best) {
+  shapes_x<NB1, NB2, NF4, NS4, NO1, NO2, NO4, DENSE, U, true, true>(mix, P, n, best);
+  shapes_x<NB1, NB2, NF4, NS4, NO1, NO2, NO4, DENSE, U, true, false>(mix, P, n, best);
+  shapes_x<NB1, NB2, NF4, NS4, NO1, NO2, NO4, DENSE, U, false, true>(mix, P, n, best);
+  shapes_x<NB1, NB2, NF4, NS4, NO1, NO2, NO4, DENSE, U, false, false>(mix, P, n, best);
+}
+
+template <int NB1, int NB2, int NF4, int NS4, int NO1, int NO2, int NO4, bool DENSE>
+static void mix_x(const char *name, const Pools &P, const std::vector<std::string> &want) {
+  if (!want.empty()) {
+    bool hit = false;
+    for (const auto &s : want) hit |= s == name;
+    if (!hit) return;
+  }
+  // about 6 GB per launch; n a multiple of 2^20 elements (every grid's
+  // chunks x 8 divide it)
+  constexpr long bpe = x_bytes_per_elem<NB1, NB2, NF4, NS4, NO1, NO2, NO4>();
+  long n = long(6e9) / bpe / (1L << 20) * (1L << 20);
+  Best best;
+  policies_x<NB1, NB2, NF4, NS4, NO1, NO2, NO4, DENSE, 1>(name, P, n, best);
+  policies_x<NB1, NB2, NF4, NS4, NO1, NO2, NO4, DENSE, 2>(name, P, n, best);
+  policies_x<NB1, NB2, NF4, NS4, NO1, NO2, NO4, DENSE, 4>(name, P, n, best);
+  policies_x<NB1, NB2, NF4, NS4, NO1, NO2, NO4, DENSE, 8>(name, P, n, best);
+  const long reads = NB1 + 2L * NB2 + 4L * NF4 + 4L * NS4;
+  std::printf("BEST %-9s R%ld W%ld %7.0f GB/s (%.1f%% of 8 TB/s)  %s\n", name, reads,
+              bpe - reads, best.gbs, best.gbs / 80.0, best.what);
+  std::fflush(stdout);
+}
+
 int main(int argc, char **argv) {
   std::vector<std::string> want;
   for (int i = 1; i < argc; ++i) want.emplace_back(argv[i]);
@@ -350,6 +605,12 @@ int main(int argc, char **argv) {
   mix<7, 7>("nd1", P, want);
   mix<70, 7>("nd64", P, want);
   mix<38, 7>("q8nd64", P, want);
+  //    int8 bf16 spill state | int8 bf16 spill | lane layout
+  mix_x<0, 16, 0, 0, 0, 0, 1, false>("norm16-x", P, want);
+  mix_x<0, 0, 1, 3, 1, 1, 0, true>("upd-x", P, want);
+  mix_x<0, 1, 0, 3, 0, 1, 0, true>("nd1-x", P, want);
+  mix_x<0, 64, 0, 3, 0, 1, 0, true>("nd64-x", P, want);
+  mix_x<64, 0, 0, 3, 1, 1, 0, true>("q8nd64-x", P, want);
   check(hipFree(P.in), "free");
   check(hipFree(P.out), "free");
   check(hipFree(P.sink), "free");
