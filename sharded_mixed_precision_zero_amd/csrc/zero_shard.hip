@@ -809,7 +809,9 @@ __device__ __forceinline__ void store_gbar(float *out, int64_t vec, int nvalid,
 // every row at once, which sustains more HBM bandwidth for this read-heavy
 // mix than a single front.  A lane's sum runs over its vectors in sweep
 // order, then a fixed butterfly over the wave and the 4 wave sums in
-// order; partial b belongs to block b.
+// order; the partial is stored at the block's slot, its position in the
+// shard, so the partials (and S) come out the same however the shard is
+// split into launches.
 template <class Src>
 __global__ void __launch_bounds__(kThreads) gnorm_partial_kernel(const NormArgs<Src> A) {
   constexpr int U = Tune<Src>::norm_unroll;
@@ -862,7 +864,7 @@ __global__ void __launch_bounds__(kThreads) gnorm_partial_kernel(const NormArgs<
   if (threadIdx.x == 0) {
     double t = 0.0;
     for (int w = 0; w < kThreads / 64; ++w) t += wsum[w];
-    A.partials[blockIdx.x] = t;
+    A.partials[slot] = t;
   }
 }
 
@@ -1224,23 +1226,41 @@ int gnorm_args_ok(zs_handle *h, double *sumsq_dev) {
 
 // a2, first sweep over one part, after the contributions were checked:
 // block partials, then the fixed-order final reduction into *sumsq_dev.
+// Launch length of the norm pass and of the wide update, in shard elements:
+// a one-shot grid over a long shard streams slower than the same work split
+// into launches of this many elements on the same stream (measured: the
+// 812.5M-element norm pass 5.07 -> 4.78 ms in launches of 2^26, the
+// N_d = 64 update over 117M elements 3.06 -> 2.90 ms in launches of 2^25).
+// Both are multiples of every block span, so only a part's last launch is
+// ragged; the one-vector update gains nothing and stays one launch.
+constexpr int64_t kNormLaunchLen = int64_t(1) << 26;
+constexpr int64_t kWideLaunchLen = int64_t(1) << 25;
+
+// a2, first sweep over one part, after the contributions were checked:
+// block partials (launches of kNormLaunchLen elements, partials in shard
+// order), then the fixed-order final reduction into *sumsq_dev.
 template <class Src>
 int launch_gnorm(int nd, float *gbar_ws, const Src &src, const Part &part, double *sumsq_dev) {
   const int64_t n = part.len;
   const hipStream_t st = part.st;
-  const int64_t blocks = norm_blocks<Src>(n);
-  NormArgs<Src> A;
-  A.src = n > 0 ? shifted(src, nd, part.off) : src;
-  A.avg = make_avg(nd);
-  A.n = n;
-  A.gbar_out = gbar_ws ? gbar_ws + part.off : nullptr;
-  A.partials = part.partials;
-  hipLaunchKernelGGL(gnorm_partial_kernel<Src>, dim3(unsigned(blocks)), dim3(kThreads), 0, st,
-                     A);
-  int rc = launched();
-  if (rc) return rc;
+  int64_t off = 0, nblocks = 0;
+  do {  // once for an empty part: its partials are zeros
+    const int64_t len = n - off < kNormLaunchLen ? n - off : kNormLaunchLen;
+    const int64_t blocks = norm_blocks<Src>(len);
+    NormArgs<Src> A;
+    A.src = len > 0 ? shifted(src, nd, part.off + off) : src;
+    A.avg = make_avg(nd);
+    A.n = len;
+    A.gbar_out = gbar_ws ? gbar_ws + part.off + off : nullptr;
+    A.partials = part.partials + nblocks;
+    hipLaunchKernelGGL(gnorm_partial_kernel<Src>, dim3(unsigned(blocks)), dim3(kThreads), 0, st,
+                       A);
+    if (int rc = launched()) return rc;
+    nblocks += blocks;
+    off += len;
+  } while (off < n);
   hipLaunchKernelGGL(gnorm_final_kernel, dim3(1), dim3(kFinalThreads), 0, st,
-                     static_cast<const double *>(part.partials), int(blocks), sumsq_dev);
+                     static_cast<const double *>(part.partials), int(nblocks), sumsq_dev);
   return launched();
 }
 
@@ -1306,8 +1326,8 @@ struct StepTime {
 };
 
 template <class Src>
-int launch_step(zs_handle *h, const Src &src, const Part &part, const StepTime &when,
-                const double *global_sumsq_dev, bool use_spill) {
+int launch_step_part(zs_handle *h, const Src &src, const Part &part, const StepTime &when,
+                     const double *global_sumsq_dev, bool use_spill) {
   const zs_desc &d = h->d;
   const int64_t n = part.len, off = part.off;
   if (n == 0) return ZS_OK;
@@ -1351,6 +1371,22 @@ int launch_step(zs_handle *h, const Src &src, const Part &part, const StepTime &
   }
 #undef ZS_LAUNCH_STEP
   return launched();
+}
+
+// The step over one part: the wide update in launches of kWideLaunchLen
+// elements, the one-vector update in one.
+template <class Src>
+int launch_step(zs_handle *h, const Src &src, const Part &part, const StepTime &when,
+                const double *global_sumsq_dev, bool use_spill) {
+  const bool wide = !use_spill && h->d.n_d >= kWideMinRows;
+  if (!wide || part.len <= kWideLaunchLen)
+    return launch_step_part(h, src, part, when, global_sumsq_dev, use_spill);
+  for (int64_t o = 0; o < part.len; o += kWideLaunchLen) {
+    const int64_t len = part.len - o < kWideLaunchLen ? part.len - o : kWideLaunchLen;
+    const Part p{part.off + o, len, part.st, part.partials};
+    if (int rc = launch_step_part(h, src, p, when, global_sumsq_dev, use_spill)) return rc;
+  }
+  return ZS_OK;
 }
 
 template <class Src>
