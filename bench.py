@@ -10,8 +10,10 @@ N_d = 16 with clipping and int8 output, the one workload that runs every
 step of the path; ``--config`` selects another.
 
 Prints one JSON line: params updated per second (``value``), the roofline
-of the dominant kernel (algorithmic bytes per launch / its mean duration
-from HIP events on the launch stream, against the 8 TB/s HBM peak), the
+of the dominant kernel (algorithmic bytes per call / the call's mean
+duration from HIP events on the launch stream, against the 8 TB/s HBM
+peak; a call of the norm pass is ceil(n / 2^26) launches, see
+``launches_per_call``), the
 whole step's GB/s both over the bytes the path moves and over the pages'
 modelled (2 N_d + 26 [+ int8 out]) B/param, the same figures for the other
 full-size workloads timed in the same run (``configs``: the 7.5B-parameter
@@ -135,10 +137,28 @@ def host_cpu() -> dict:
     return {"nproc": os.cpu_count(), "usable_cpus": usable, "model": model}
 
 
+def launches_per_call(w, kernel: str, spill: bool) -> int:
+    """Launches of the timed kernel that one call of the library queues
+    (zero_shard.h): the norm pass's partial-sum kernel ceil(n /
+    ZS_NORM_LAUNCH_LEN) times (plus its final reduction, ~20 us, timed with
+    it but not counted here); an update that reads ZS_WIDE_MIN_ROWS rows or
+    more ceil(n / ZS_WIDE_LAUNCH_LEN) times; any other update once."""
+    import sharded_mixed_precision_zero_amd as Z
+
+    n = max(w.shard_len, 1)
+    if kernel == "gnorm":
+        return -(-n // Z.ZS_NORM_LAUNCH_LEN)
+    reads_rows = not (w.max_norm > 0 and spill)
+    if reads_rows and w.n_d >= Z.ZS_WIDE_MIN_ROWS:
+        return -(-n // Z.ZS_WIDE_LAUNCH_LEN)
+    return 1
+
+
 def measured_traffic(w, kernel: str) -> float | None:
-    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
-    summary for this workload, if the kernel source is the one the counters
-    were taken on (else None: the counters are stale)."""
+    """HBM bytes per call of `kernel` (all its launches in one call) from the
+    committed rocprofv3 counter summary for this workload, if the kernel
+    source is the one the counters were taken on (else None: the counters
+    are stale)."""
     path = os.path.join(ROOT, "profiles", f"hbm_counters_{w.name}.md")
     src = os.path.join(ROOT, "sharded_mixed_precision_zero_amd", "csrc", "zero_shard.hip")
     if not os.path.exists(path):
@@ -151,7 +171,7 @@ def measured_traffic(w, kernel: str) -> float | None:
         f = line.strip().strip("`").split()
         if len(f) == 2 and f[0] == "source_sha256":
             rec = f[1]
-        if len(f) == 3 and f[0] == "traffic_bytes_per_launch":
+        if len(f) == 3 and f[0] == "traffic_bytes_per_call":
             tr[f[1]] = float(f[2])
     if rec != sha:
         return None
@@ -757,7 +777,8 @@ def main() -> int:
         "hbm": summary(w, head)["hbm"],
         "roofline": {"bound": "hbm", "kernel": kernel_names[dominant], "achieved": ach,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
-                     "traffic": traffic},
+                     "traffic": traffic, "per": "call",
+                     "launches_per_call": head["per_kernel"][dominant]["launches_per_call"]},
         "ceiling": None if best is None else {
             "probe": "tests/native/hbm_probe, run in this bench: best over its access shapes "
                      "for each launch's read:write mix",
@@ -885,6 +906,7 @@ def measure(w, args, spill: bool, bucket_len: int) -> dict:
         per_kernel[k] = {"mean_ms": round(ms, 4), "median_ms": round(srt[len(srt) // 2], 4),
                          "min_ms": round(srt[0], 4), "max_ms": round(srt[-1], 4),
                          "bytes_per_param": kb[k],
+                         "launches_per_call": None if bucket_len else launches_per_call(w, k, spill),
                          "GBps": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4)}
         _eprint(f"[bench] {w.name} {k}: {ms:.4f} ms, {kb[k]:.3f} B/param, {gbs:.1f} GB/s "
                 f"({100 * gbs / HBM_PEAK_GBS:.1f}% of 8 TB/s)")

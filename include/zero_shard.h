@@ -86,6 +86,16 @@ typedef enum zs_status {
 
 #define ZS_MAX_ND 64 /* most contributions one call can average */
 
+/* How the work of a call is split into kernel launches (on the call's
+ * stream, in order; the split changes no result).  The norm pass over n
+ * elements (the shard, or one bucket) queues ceil(n / ZS_NORM_LAUNCH_LEN)
+ * partial-sum launches and one final reduction.  An update that reads
+ * ZS_WIDE_MIN_ROWS or more contribution rows (no spill) queues
+ * ceil(n / ZS_WIDE_LAUNCH_LEN) launches; any other update one. */
+#define ZS_NORM_LAUNCH_LEN (INT64_C(1) << 26)
+#define ZS_WIDE_LAUNCH_LEN (INT64_C(1) << 25)
+#define ZS_WIDE_MIN_ROWS 16
+
 typedef struct zs_desc {
   /* partition geometry */
   int64_t phi;       /* parameters in the whole flat buffer, >= 0           */
@@ -148,7 +158,8 @@ int zero_shard_gnorm(zs_handle *h, const zs_bf16 *const *contrib, double *sumsq_
  * beyond).  Every call on one GPU uses that GPU's one array: calls that
  * overlap on one GPU (other streams, other threads) race and must be
  * ordered by the caller; the partials need no clearing (each call writes
- * all it reads).  Queues two kernel launches on d->stream and nothing else.
+ * all it reads).  Queues ceil(shard_len / ZS_NORM_LAUNCH_LEN) + 1 kernel
+ * launches (at least two) on d->stream and nothing else.
  * Errors: ZS_EINVAL, ZS_EALIGN, ZS_ETOOBIG, ZS_EDEVICE, ZS_EHIP. */
 int zero_shard_gnorm_noalloc(const zs_desc *d, const zs_bf16 *const *contrib,
                              double *sumsq_dev);

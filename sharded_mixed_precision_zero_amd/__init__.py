@@ -20,6 +20,10 @@ LIB_PATH = os.path.join(_HERE, "libzeroshard.so")
 ZS_OK, ZS_EINVAL, ZS_EALIGN, ZS_ENOMEM, ZS_EHIP, ZS_EDEVICE, ZS_ESTATE, ZS_ETOOBIG = (
     0, -1, -2, -3, -4, -5, -6, -7)
 ZS_MAX_ND = 64
+# how a call's work is split into kernel launches (zero_shard.h)
+ZS_NORM_LAUNCH_LEN = 1 << 26
+ZS_WIDE_LAUNCH_LEN = 1 << 25
+ZS_WIDE_MIN_ROWS = 16
 QUANT_BLOCKS = (32, 64, 128, 256, 512)
 
 if not os.path.exists(LIB_PATH):

@@ -62,12 +62,6 @@ constexpr int kRowGroup = ZS_ROW_GROUP;  // contribution rows loaded together (u
 #define ZS_NORM_ROW_GROUP 4
 #endif
 
-#ifndef ZS_NORM_FRONTS
-#define ZS_NORM_FRONTS 2
-#endif
-// The norm pass's grid walks the shard as this many fronts at once (see
-// gnorm_partial_kernel).
-constexpr int kNormFronts = ZS_NORM_FRONTS;
 #ifndef ZS_NORM_UNROLL
 #define ZS_NORM_UNROLL 8
 #endif
@@ -724,9 +718,6 @@ __device__ __forceinline__ AdamConst step_consts(const StepArgs<Src> &A) {
   return k;
 }
 
-#ifndef ZS_WIDE_MIN_ROWS
-#define ZS_WIDE_MIN_ROWS 16
-#endif
 constexpr int kWideMinRows = ZS_WIDE_MIN_ROWS;  // rows from which the update goes wide
 
 // a1 + a2 (apply) + a3 + a4 (+ a5 when QL > 0).  Each wave owns U
@@ -803,15 +794,11 @@ __device__ __forceinline__ void store_gbar(float *out, int64_t vec, int nvalid,
 // a2, first kernel: block partial sums of gbar^2 (binary64).  The grid is
 // fixed by n alone: one pass, each block 4 waves x one sweep of 64*U
 // (U per contribution format) consecutive lane-vectors (lane l takes
-// v0+l, v0+64+l, ...).  The blocks are laid out as kNormFronts contiguous
-// stretches of the shard taken in turn (block b works in stretch b mod
-// kNormFronts), so that the chip streams from several separated regions of
-// every row at once, which sustains more HBM bandwidth for this read-heavy
-// mix than a single front.  A lane's sum runs over its vectors in sweep
-// order, then a fixed butterfly over the wave and the 4 wave sums in
-// order; the partial is stored at the block's slot, its position in the
-// shard, so the partials (and S) come out the same however the shard is
-// split into launches.
+// v0+l, v0+64+l, ...), block b the b-th stretch of the launch.  A lane's
+// sum runs over its vectors in sweep order, then a fixed butterfly over the
+// wave and the 4 wave sums in order; partial b belongs to block b, and the
+// launches of a part write consecutive runs of partials, so the partials
+// (and S) are in shard order however the part is split into launches.
 template <class Src>
 __global__ void __launch_bounds__(kThreads) gnorm_partial_kernel(const NormArgs<Src> A) {
   constexpr int U = Tune<Src>::norm_unroll;
@@ -820,9 +807,7 @@ __global__ void __launch_bounds__(kThreads) gnorm_partial_kernel(const NormArgs<
   const int wave = threadIdx.x >> 6;
   const int64_t nvec = (A.n + kVec - 1) / kVec;
   const int64_t nfull = A.n / kVec;
-  const int64_t per_front = int64_t(gridDim.x) / kNormFronts;  // grid: a multiple of it
-  const int64_t slot = int64_t(blockIdx.x % kNormFronts) * per_front + blockIdx.x / kNormFronts;
-  const int64_t wb = (slot * (kThreads / 64) + wave) * span;
+  const int64_t wb = (int64_t(blockIdx.x) * (kThreads / 64) + wave) * span;
   double acc = 0.0;
   if (wb < nvec) {
     if (wb + span <= nfull) {
@@ -864,7 +849,7 @@ __global__ void __launch_bounds__(kThreads) gnorm_partial_kernel(const NormArgs<
   if (threadIdx.x == 0) {
     double t = 0.0;
     for (int w = 0; w < kThreads / 64; ++w) t += wsum[w];
-    A.partials[slot] = t;
+    A.partials[blockIdx.x] = t;
   }
 }
 
@@ -1114,15 +1099,13 @@ int64_t grid_blocks(const zs_handle *h, int64_t nvec, int unroll) {
   return need < cap ? need : cap;
 }
 
-// Blocks of the norm pass over n elements: one per 4*64*U lane-vectors,
-// rounded up to a multiple of the front count.
+// Blocks of the norm pass over n elements: one per 4*64*U lane-vectors.
 template <class Src>
 int64_t norm_blocks(int64_t n) {
   const int64_t nvec = (n + kVec - 1) / kVec;
   const int64_t per_block = int64_t(kThreads) * Tune<Src>::norm_unroll;
-  int64_t b = (nvec + per_block - 1) / per_block;
-  if (b < 1) b = 1;
-  return (b + kNormFronts - 1) / kNormFronts * kNormFronts;
+  const int64_t b = (nvec + per_block - 1) / per_block;
+  return b < 1 ? 1 : b;
 }
 
 // Partials a norm pass over n elements needs, for either contribution format.
@@ -1226,15 +1209,19 @@ int gnorm_args_ok(zs_handle *h, double *sumsq_dev) {
 
 // a2, first sweep over one part, after the contributions were checked:
 // block partials, then the fixed-order final reduction into *sumsq_dev.
-// Launch length of the norm pass and of the wide update, in shard elements:
-// a one-shot grid over a long shard streams slower than the same work split
-// into launches of this many elements on the same stream (measured: the
-// 812.5M-element norm pass 5.07 -> 4.78 ms in launches of 2^26, the
-// N_d = 64 update over 117M elements 3.06 -> 2.90 ms in launches of 2^25).
-// Both are multiples of every block span, so only a part's last launch is
-// ragged; the one-vector update gains nothing and stays one launch.
-constexpr int64_t kNormLaunchLen = int64_t(1) << 26;
-constexpr int64_t kWideLaunchLen = int64_t(1) << 25;
+// Launch length of the norm pass and of the wide update, in shard elements
+// (the values zero_shard.h documents): a one-shot grid over a long shard
+// streams slower than the same work split into launches of this many
+// elements on the same stream (measured: the 812.5M-element norm pass
+// 5.07 -> 4.78 ms in launches of 2^26, the N_d = 64 update over 117M
+// elements 3.06 -> 2.90 ms in launches of 2^25).  Both are multiples of
+// every block span, so only a part's last launch is ragged; the one-vector
+// update gains nothing and stays one launch.
+constexpr int64_t kNormLaunchLen = ZS_NORM_LAUNCH_LEN;
+constexpr int64_t kWideLaunchLen = ZS_WIDE_LAUNCH_LEN;
+static_assert(kNormLaunchLen % (int64_t(kThreads) * kVec * ZS_NORM_UNROLL) == 0 &&
+                  kWideLaunchLen % (int64_t(512) * ZS_WIDE_UNROLL) == 0,
+              "launch lengths must be whole blocks");
 
 // a2, first sweep over one part, after the contributions were checked:
 // block partials (launches of kNormLaunchLen elements, partials in shard

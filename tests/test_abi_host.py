@@ -57,6 +57,20 @@ def test_descriptor_layout_matches_header():
         assert int(got[f]) == getattr(Z.zs_desc, f).offset, f
 
 
+def test_constants_match_header():
+    prog = ["#include <stdio.h>", '#include "zero_shard.h"', "int main(void) {",
+            'printf("%d %lld %lld %d\\n", ZS_MAX_ND, (long long)ZS_NORM_LAUNCH_LEN,',
+            "       (long long)ZS_WIDE_LAUNCH_LEN, ZS_WIDE_MIN_ROWS);", "return 0; }"]
+    with tempfile.TemporaryDirectory() as d:
+        src, exe = os.path.join(d, "c.c"), os.path.join(d, "c")
+        open(src, "w").write("\n".join(prog))
+        subprocess.run(["gcc", "-std=c99", "-I", os.path.dirname(HEADER), src, "-o", exe],
+                       check=True)
+        out = subprocess.run([exe], capture_output=True, text=True, check=True).stdout.split()
+    assert [int(x) for x in out] == [Z.ZS_MAX_ND, Z.ZS_NORM_LAUNCH_LEN, Z.ZS_WIDE_LAUNCH_LEN,
+                                     Z.ZS_WIDE_MIN_ROWS]
+
+
 def test_partition_geometry():
     for w in S.WORKLOADS:
         assert Z.zero_shard_len(w.phi, w.n_d, w.r) == w.shard_len
