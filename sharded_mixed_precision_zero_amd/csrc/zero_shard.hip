@@ -684,7 +684,9 @@ __device__ __forceinline__ void update_dense(const StepArgs<Src> &A, const AdamC
 }
 
 // a1 (rows) or the spilled gradient, then the update, on the full chunk c in
-// the dense layout, one chunk per wave.
+// the dense layout, one chunk per wave.  The state is loaded after the
+// gradient is formed: held across the row loop it would not fit the 96
+// registers of the 5-wave form (the compiler spills it to scratch).
 template <int QL, class Src>
 __device__ __forceinline__ void step_chunk_dense(const StepArgs<Src> &A, const AdamConst &k,
                                                  int64_t c, int lane, double coef) {
@@ -762,7 +764,7 @@ __global__ void __launch_bounds__(kThreads)
     if constexpr (U == 1) {
       step_chunk_dense<QL>(A, k, wb / 64, lane, coef);
     } else {
-      float g[U][kVec];
+      float g[U][kVec];  // launched only without a spill: the rows are read
       reduce_dense<U, Tune<Src>::wide_group>(A.src, A.avg, wb / 64, lane, g);
 #pragma unroll
       for (int u = 0; u < U; ++u) {
