@@ -102,10 +102,10 @@ struct Q8Rows {
 };
 
 #ifndef ZS_Q8_WIDE_UNROLL
-#define ZS_Q8_WIDE_UNROLL 4
+#define ZS_Q8_WIDE_UNROLL 2
 #endif
 #ifndef ZS_Q8_WIDE_GROUP
-#define ZS_Q8_WIDE_GROUP 2
+#define ZS_Q8_WIDE_GROUP 4
 #endif
 #ifndef ZS_Q8_NORM_UNROLL
 #define ZS_Q8_NORM_UNROLL 2
