@@ -1,6 +1,7 @@
 """Host-side pieces of bench.py (no GPU): the stream probe's mix for each
 launch, the parse of the probe's summary lines, each launch's fraction of its
-mix's best, and the single-GPU refusal."""
+mix's best, the launches one call of each timed kernel queues, and the
+single-GPU refusal."""
 
 import subprocess
 import sys
@@ -38,6 +39,21 @@ def test_probe_summary_parse():
 def test_probe_mix_per_launch(name, spill, want):
     w = S.by_name(name)
     assert {k: bench.probe_mix(w, k, spill) for k in bench.kernel_bytes(w, spill)} == want
+
+
+@pytest.mark.parametrize("name,spill,want", [
+    # the 812.5M-element norm pass: 12 launches of 2^26 and one of 7,193,632
+    ("13B-nd16-clip-int8", True, {"gnorm": 13, "step": 1}),
+    # clipping without the spill re-reads the 16 rows: the wide update
+    ("13B-nd16-clip-int8", False, {"gnorm": 13, "step": 25}),
+    ("7.5B-nd64", True, {"step": 4}),
+    ("7.5B-nd64-zeropp", True, {"step": 4}),
+    ("13B-nd1-stage0", True, {"step": 1}),
+    ("tiny-zero1", True, {"step": 1}),
+])
+def test_launches_per_call(name, spill, want):
+    w = S.by_name(name)
+    assert {k: bench.launches_per_call(w, k, spill) for k in bench.kernel_bytes(w, spill)} == want
 
 
 def test_probe_mix_traffic_matches_launch_bytes():
