@@ -141,15 +141,19 @@ def launches_per_call(w, kernel: str, spill: bool) -> int:
     """Launches of the timed kernel that one call of the library queues
     (zero_shard.h): the norm pass's partial-sum kernel ceil(n /
     ZS_NORM_LAUNCH_LEN) times (plus its final reduction, ~20 us, timed with
-    it but not counted here); an update that reads ZS_WIDE_MIN_ROWS rows or
-    more ceil(n / ZS_WIDE_LAUNCH_LEN) times; any other update once."""
+    it but not counted here); an update that reads the rows in its wide form
+    (ZS_WIDE_MIN_ROWS bf16 rows or more, ZS_WIDE_MIN_ROWS_QUANT with int8
+    output, ZS_WIDE_MIN_ROWS_Q8 int8 rows) ceil(n / ZS_WIDE_LAUNCH_LEN)
+    times; any other update once."""
     import sharded_mixed_precision_zero_amd as Z
 
     n = max(w.shard_len, 1)
     if kernel == "gnorm":
         return -(-n // Z.ZS_NORM_LAUNCH_LEN)
     reads_rows = not (w.max_norm > 0 and spill)
-    if reads_rows and w.n_d >= Z.ZS_WIDE_MIN_ROWS:
+    from_rows = (Z.ZS_WIDE_MIN_ROWS_Q8 if w.contrib_block else
+                 Z.ZS_WIDE_MIN_ROWS_QUANT if w.quant_block else Z.ZS_WIDE_MIN_ROWS)
+    if reads_rows and w.n_d >= from_rows:
         return -(-n // Z.ZS_WIDE_LAUNCH_LEN)
     return 1
 

@@ -89,12 +89,16 @@ typedef enum zs_status {
 /* How the work of a call is split into kernel launches (on the call's
  * stream, in order; the split changes no result).  The norm pass over n
  * elements (the shard, or one bucket) queues ceil(n / ZS_NORM_LAUNCH_LEN)
- * partial-sum launches and one final reduction.  An update that reads
- * ZS_WIDE_MIN_ROWS or more contribution rows (no spill) queues
- * ceil(n / ZS_WIDE_LAUNCH_LEN) launches; any other update one. */
+ * partial-sum launches and one final reduction.  An update that reads the
+ * contribution rows (no spill) runs in its wide form, as
+ * ceil(n / ZS_WIDE_LAUNCH_LEN) launches, from ZS_WIDE_MIN_ROWS bf16 rows
+ * (ZS_WIDE_MIN_ROWS_QUANT when it also writes int8) or ZS_WIDE_MIN_ROWS_Q8
+ * int8 rows; any other update is one launch. */
 #define ZS_NORM_LAUNCH_LEN (INT64_C(1) << 26)
 #define ZS_WIDE_LAUNCH_LEN (INT64_C(1) << 25)
-#define ZS_WIDE_MIN_ROWS 16
+#define ZS_WIDE_MIN_ROWS 18
+#define ZS_WIDE_MIN_ROWS_QUANT 32
+#define ZS_WIDE_MIN_ROWS_Q8 16
 
 typedef struct zs_desc {
   /* partition geometry */

@@ -23,7 +23,9 @@ ZS_MAX_ND = 64
 # how a call's work is split into kernel launches (zero_shard.h)
 ZS_NORM_LAUNCH_LEN = 1 << 26
 ZS_WIDE_LAUNCH_LEN = 1 << 25
-ZS_WIDE_MIN_ROWS = 16
+ZS_WIDE_MIN_ROWS = 18
+ZS_WIDE_MIN_ROWS_QUANT = 32
+ZS_WIDE_MIN_ROWS_Q8 = 16
 QUANT_BLOCKS = (32, 64, 128, 256, 512)
 
 if not os.path.exists(LIB_PATH):

@@ -720,8 +720,6 @@ __device__ __forceinline__ AdamConst step_consts(const StepArgs<Src> &A) {
   return k;
 }
 
-constexpr int kWideMinRows = ZS_WIDE_MIN_ROWS;  // rows from which the update goes wide
-
 // a1 + a2 (apply) + a3 + a4 (+ a5 when QL > 0).  Each wave owns U
 // consecutive 512-element chunks per iteration, in the dense layout.  U = 1:
 // one chunk, state, gradient and outputs together.  U > 1 (many
@@ -1314,6 +1312,22 @@ struct StepTime {
   const double *dyn;
 };
 
+// Whether an update over n_d contribution rows (no spill) takes the wide
+// form: from 18 bf16 rows, 32 when it also quantizes, 16 int8 rows (the
+// values zero_shard.h documents).  Measured in one process on the same
+// buffers, each form against the other: bf16 rows unquantized, the one-chunk
+// form 0.5-2.4% faster at 16-17 rows, the wide form 0.5% at 18-20, 3.6% at
+// 24, 9% at 32; quantizing, the one-chunk form 6.6-14% faster at 16-24
+// rows, the wide form 1% at 32 and 14% at 64; int8 rows, the wide form
+// 3.7% faster at 16.
+template <class Src>
+bool wide_update(const zs_desc &d, bool use_spill) {
+  const int from = !kBf16Src<Src>  ? ZS_WIDE_MIN_ROWS_Q8
+                   : d.quant_block ? ZS_WIDE_MIN_ROWS_QUANT
+                                   : ZS_WIDE_MIN_ROWS;
+  return !use_spill && d.n_d >= from;
+}
+
 template <class Src>
 int launch_step_part(zs_handle *h, const Src &src, const Part &part, const StepTime &when,
                      const double *global_sumsq_dev, bool use_spill) {
@@ -1338,7 +1352,7 @@ int launch_step_part(zs_handle *h, const Src &src, const Part &part, const StepT
   A.scales = d.q_scales ? d.q_scales + off / (d.quant_block ? d.quant_block : 1) : nullptr;
   const hipStream_t st = part.st;
   const int64_t nvec = (n + kVec - 1) / kVec;
-  const bool wide = !A.gbar && d.n_d >= kWideMinRows;
+  const bool wide = wide_update<Src>(d, use_spill);
   constexpr int WU = Tune<Src>::wide_unroll;
   const dim3 grid(unsigned(grid_blocks(h, nvec, wide ? WU : 1))), block(kThreads);
 #define ZS_LAUNCH_STEP(QL)                                                            \
@@ -1367,7 +1381,7 @@ int launch_step_part(zs_handle *h, const Src &src, const Part &part, const StepT
 template <class Src>
 int launch_step(zs_handle *h, const Src &src, const Part &part, const StepTime &when,
                 const double *global_sumsq_dev, bool use_spill) {
-  const bool wide = !use_spill && h->d.n_d >= kWideMinRows;
+  const bool wide = wide_update<Src>(h->d, use_spill);
   if (!wide || part.len <= kWideLaunchLen)
     return launch_step_part(h, src, part, when, global_sumsq_dev, use_spill);
   for (int64_t o = 0; o < part.len; o += kWideLaunchLen) {

@@ -59,8 +59,9 @@ def test_descriptor_layout_matches_header():
 
 def test_constants_match_header():
     prog = ["#include <stdio.h>", '#include "zero_shard.h"', "int main(void) {",
-            'printf("%d %lld %lld %d\\n", ZS_MAX_ND, (long long)ZS_NORM_LAUNCH_LEN,',
-            "       (long long)ZS_WIDE_LAUNCH_LEN, ZS_WIDE_MIN_ROWS);", "return 0; }"]
+            'printf("%d %lld %lld %d %d %d\\n", ZS_MAX_ND, (long long)ZS_NORM_LAUNCH_LEN,',
+            "       (long long)ZS_WIDE_LAUNCH_LEN, ZS_WIDE_MIN_ROWS, ZS_WIDE_MIN_ROWS_QUANT,",
+            "       ZS_WIDE_MIN_ROWS_Q8);", "return 0; }"]
     with tempfile.TemporaryDirectory() as d:
         src, exe = os.path.join(d, "c.c"), os.path.join(d, "c")
         open(src, "w").write("\n".join(prog))
@@ -68,7 +69,8 @@ def test_constants_match_header():
                        check=True)
         out = subprocess.run([exe], capture_output=True, text=True, check=True).stdout.split()
     assert [int(x) for x in out] == [Z.ZS_MAX_ND, Z.ZS_NORM_LAUNCH_LEN, Z.ZS_WIDE_LAUNCH_LEN,
-                                     Z.ZS_WIDE_MIN_ROWS]
+                                     Z.ZS_WIDE_MIN_ROWS, Z.ZS_WIDE_MIN_ROWS_QUANT,
+                                     Z.ZS_WIDE_MIN_ROWS_Q8]
 
 
 def test_partition_geometry():

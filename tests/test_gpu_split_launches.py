@@ -28,16 +28,17 @@ CASES = [
     #  launch length, bucket length or 0)
     ("bf16 norm + clipped update", "13B-nd16-clip-int8", LN + 1029, 16, 0, 256, 1.0, LN, 0),
     ("int8-row norm + clipped update", "7.5B-nd64-zeropp", LN + 77, 4, 64, 0, 0.5, LN, 0),
-    ("bf16 wide update", "7.5B-nd64", 2 * LW + 333, 16, 0, 0, 0.0, LW, 0),
+    ("bf16 wide update", "7.5B-nd64", 2 * LW + 333, 24, 0, 0, 0.0, LW, 0),
+    ("bf16 wide update, int8 out", "7.5B-nd64", LW + 99, 32, 0, 128, 0.0, LW, 0),
     ("int8-row wide update", "7.5B-nd64-zeropp", 2 * LW + 4099, 16, 256, 256, 0.0, LW, 0),
     # whole launches only, no ragged last one
     ("bf16 norm, two whole launches", "13B-nd16-clip-int8", 2 * LN, 8, 0, 256, 1.0, LN, 0),
-    ("bf16 wide update, two whole launches", "7.5B-nd64", 2 * LW, 16, 0, 0, 0.0, LW, 0),
+    ("bf16 wide update, two whole launches", "7.5B-nd64", 2 * LW, 24, 0, 0, 0.0, LW, 0),
     # buckets longer than one launch: the first bucket's norm pass is two launches
     ("bf16 bucketed norm + clipped update", "13B-nd16-clip-int8", LN + LW + 333, 16, 0, 256, 1.0,
      LN, LN + 512),
     # the first bucket's wide update is two launches
-    ("bf16 bucketed wide update", "7.5B-nd64", LW + LW // 2 + 77, 16, 0, 0, 0.0, LW, LW + 512),
+    ("bf16 bucketed wide update", "7.5B-nd64", LW + LW // 2 + 77, 24, 0, 0, 0.0, LW, LW + 512),
 ]
 
 
