@@ -1,6 +1,6 @@
 """Calls whose work the library splits into several kernel launches: the
 norm pass runs in launches of ZS_NORM_LAUNCH_LEN shard elements, an update
-that reads 16 or more contribution rows in launches of ZS_WIDE_LAUNCH_LEN.
+in its wide form (many contribution rows) in launches of ZS_WIDE_LAUNCH_LEN.
 S is checked against the oracle over the whole shard, and the spill and the
 updated state on windows that straddle the launch boundaries, the head and
 the tail, for bf16 and int8 contributions (tolerances of tests/_parity.py).
