@@ -88,3 +88,23 @@ def test_more_than_one_gpu_is_refused():
                        text=True, timeout=120)
     assert p.returncode == 2
     assert "one GPU" in p.stderr
+
+
+def test_measured_traffic_reads_the_committed_counters():
+    """roofline.traffic: the HBM bytes per call of the dominant kernel from
+    the committed counter summary, only while its source hash is the
+    library's (then within 1% of the algorithmic bytes of a call)."""
+    import hashlib
+    import os
+    import re
+
+    w = S.by_name("13B-nd16-clip-int8")
+    path = os.path.join(bench.ROOT, "profiles", "hbm_counters_13B-nd16-clip-int8.md")
+    src = os.path.join(bench.ROOT, "sharded_mixed_precision_zero_amd", "csrc", "zero_shard.hip")
+    rec = re.search(r"source_sha256 (\w+)", open(path).read()).group(1)
+    got = bench.measured_traffic(w, "gnorm_partial_kernel")
+    if rec != hashlib.sha256(open(src, "rb").read()).hexdigest():
+        assert got is None
+        return
+    algo = bench.kernel_bytes(w, True)["gnorm"] * w.shard_len
+    assert got is not None and abs(got / algo - 1.0) < 0.01
