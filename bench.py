@@ -647,6 +647,10 @@ def main() -> int:
     ap.add_argument("--extra-configs", default="7.5B-nd64,7.5B-nd64-zeropp,13B-nd1-stage0",
                     help="other workloads timed in the same run and reported under 'configs'")
     ap.add_argument("--no-extra-configs", action="store_true")
+    ap.add_argument("--layout", choices=("separate", "spaced"), default="separate",
+                    help="caller's placement of the shard's state, spill and output arrays: "
+                         "one allocation per array (default), or each at the start of its own "
+                         "16 GiB slot of one arena")
     ap.add_argument("--cold-cache", type=int, default=0, metavar="MIB",
                     help="write a MIB-MiB scratch buffer between timed steps, so that no step "
                          "finds the previous one's data in the caches; ms_per_step and value "
@@ -773,6 +777,7 @@ def main() -> int:
                    "quant_block": w.quant_block, "grad_spill": bool(spill and w.max_norm > 0),
                    "bucket_len": bucket_len or None,
                    "cold_cache_MiB": args.cold_cache or None,
+                   "layout": args.layout,
                    "bucket_streams": args.bucket_streams if bucket_len else None,
                    "storage": {"contributions": "int8" if w.contrib_block else "bf16",
                                "state": "fp32", "params_out": "bf16",
@@ -833,8 +838,9 @@ def measure(w, args, spill: bool, bucket_len: int) -> dict:
 
     n = w.shard_len
     _eprint(f"[bench] workload {w.name}: shard {n} of phi {w.phi}, n_d {w.n_d}, "
-            f"clip {w.max_norm}, int8 block {w.quant_block}, spill {spill and w.max_norm > 0}")
-    g = GpuShard(w, spill=spill)
+            f"clip {w.max_norm}, int8 block {w.quant_block}, spill {spill and w.max_norm > 0}, "
+            f"layout {args.layout}")
+    g = GpuShard(w, spill=spill, layout=args.layout)
     g.init_state()
     g.fill_grads(1)  # resident contributions, reused by every timed step
     torch.cuda.synchronize()

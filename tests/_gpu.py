@@ -36,10 +36,33 @@ def row_stride(n: int) -> int:
     return (n + 127) // 128 * 128 + 640
 
 
+SLOT_BYTES = 16 << 30  # the spaced layout's slot: arrays start at least this far apart
+
+
+def spaced_slots(nbytes: list[int], slot: int = SLOT_BYTES) -> tuple[list[int], int] | None:
+    """Offsets of arrays of the given byte sizes in one arena, each at the
+    start of its own slot of `slot` bytes, and the arena's size; None when an
+    array does not fit a slot (such arrays are allocated on their own, which
+    places them at least their own size apart)."""
+    if any(b > slot for b in nbytes):
+        return None
+    return [i * slot for i in range(len(nbytes))], len(nbytes) * slot
+
+
 class GpuShard:
+    """One shard's device buffers and its library handle.
+
+    layout "separate" (default): one allocation per array.  layout
+    "spaced": the state, spill and output arrays in one arena, each at the
+    start of its own 16 GiB slot (arrays larger than a slot keep one
+    allocation each).  The kernels and results are the same either way; the
+    layouts differ only in where the caller's arrays sit in HBM, which moves
+    the update's streaming rate (the benchmark's --layout)."""
+
     def __init__(self, w: S.Workload, n: int | None = None, i0: int = 0, *, spill: bool = True,
                  quant_block: int | None = None, n_d: int | None = None, phi: int | None = None,
-                 r: int | None = None, bias_correction: bool = True, stream=None):
+                 r: int | None = None, bias_correction: bool = True, stream=None,
+                 layout: str = "separate"):
         import torch
 
         self.torch = torch
@@ -51,15 +74,31 @@ class GpuShard:
         self.clip = w.max_norm > 0
         n_ = self.n
         f32 = dict(dtype=torch.float32, device=DEV)
-        self.master = torch.empty(n_, **f32)
-        self.m = torch.empty(n_, **f32)
-        self.v = torch.empty(n_, **f32)
-        self.p = torch.empty(n_, dtype=torch.int16, device=DEV)
-        self.codes = self.scales = None
+        specs = [("master", n_, torch.float32), ("m", n_, torch.float32),
+                 ("v", n_, torch.float32), ("p", n_, torch.int16)]
         if self.qb:
-            self.codes = torch.empty(n_, dtype=torch.int8, device=DEV)
-            self.scales = torch.empty((n_ + self.qb - 1) // self.qb, **f32)
-        self.gbar_ws = torch.empty(n_, **f32) if (self.clip and spill) else None
+            specs += [("codes", n_, torch.int8),
+                      ("scales", (n_ + self.qb - 1) // self.qb, torch.float32)]
+        if self.clip and spill:
+            specs.append(("gbar_ws", n_, torch.float32))
+        if layout not in ("separate", "spaced"):
+            raise ValueError(f"layout {layout!r}")
+        self.layout = layout
+        self.arena = None
+        sizes = [k * torch.empty(0, dtype=dt).element_size() for _, k, dt in specs]
+        plan = spaced_slots(sizes) if layout == "spaced" else None
+        if plan is not None:
+            offs, total = plan
+            self.arena = torch.empty(total, dtype=torch.uint8, device=DEV)
+            for (nm, k, dt), off, nb in zip(specs, offs, sizes):
+                setattr(self, nm, self.arena[off: off + nb].view(dt))
+        else:
+            for nm, k, dt in specs:
+                setattr(self, nm, torch.empty(k, dtype=dt, device=DEV))
+        if not self.qb:
+            self.codes = self.scales = None
+        if not (self.clip and spill):
+            self.gbar_ws = None
         self.sumsq = torch.zeros(1, dtype=torch.float64, device=DEV)
         self.stride = row_stride(n_)
         self.cb = w.contrib_block

@@ -108,3 +108,24 @@ def test_measured_traffic_reads_the_committed_counters():
         return
     algo = bench.kernel_bytes(w, True)["gnorm"] * w.shard_len
     assert got is not None and abs(got / algo - 1.0) < 0.01
+
+
+def test_spaced_layout_slots():
+    """The benchmark's spaced layout: every state, spill and output array at
+    the start of its own 16 GiB slot; arrays larger than a slot (the 13B
+    stage-0 buffer) keep one allocation each; the arena and the contribution
+    rows fit the 288 GB of one MI355X."""
+    from tests._gpu import SLOT_BYTES, row_stride, spaced_slots
+
+    w = S.by_name("13B-nd16-clip-int8")
+    n = w.shard_len
+    sizes = [4 * n, 4 * n, 4 * n, 2 * n, n, 4 * -(-n // w.quant_block), 4 * n]
+    offs, total = spaced_slots(sizes)
+    assert offs == [i * SLOT_BYTES for i in range(len(sizes))]
+    assert all(b <= SLOT_BYTES for b in sizes)
+    assert all(o % SLOT_BYTES == 0 for o in offs)
+    rows = 2 * ((w.n_d - 1) * row_stride(n) + n)
+    assert total + rows < 288e9
+    big = S.by_name("13B-nd1-stage0")
+    assert spaced_slots([4 * big.shard_len, 2 * big.shard_len]) is None
+    assert spaced_slots([]) == ([], 0)
