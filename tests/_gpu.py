@@ -54,15 +54,15 @@ class GpuShard:
 
     layout "separate" (default): one allocation per array.  layout
     "spaced": the state, spill and output arrays in one arena, each at the
-    start of its own 16 GiB slot (arrays larger than a slot keep one
-    allocation each).  The kernels and results are the same either way; the
+    start of its own slot of slot_bytes (16 GiB; arrays larger than a slot
+    keep one allocation each).  The kernels and results are the same either way; the
     layouts differ only in where the caller's arrays sit in HBM, which moves
     the update's streaming rate (the benchmark's --layout)."""
 
     def __init__(self, w: S.Workload, n: int | None = None, i0: int = 0, *, spill: bool = True,
                  quant_block: int | None = None, n_d: int | None = None, phi: int | None = None,
                  r: int | None = None, bias_correction: bool = True, stream=None,
-                 layout: str = "separate"):
+                 layout: str = "separate", slot_bytes: int = SLOT_BYTES):
         import torch
 
         self.torch = torch
@@ -86,7 +86,7 @@ class GpuShard:
         self.layout = layout
         self.arena = None
         sizes = [k * torch.empty(0, dtype=dt).element_size() for _, k, dt in specs]
-        plan = spaced_slots(sizes) if layout == "spaced" else None
+        plan = spaced_slots(sizes, slot_bytes) if layout == "spaced" else None
         if plan is not None:
             offs, total = plan
             self.arena = torch.empty(total, dtype=torch.uint8, device=DEV)

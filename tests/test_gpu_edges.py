@@ -36,12 +36,12 @@ def _variant(base: str, **kw) -> S.Workload:
 
 
 def _run_pair(w: S.Workload, n: int, steps: int, *, bias_correction=True, spill=True,
-              poison=None):
+              poison=None, **shard_kw):
     """Run `steps` steps of workload w over an n-element unpartitioned shard on
     the GPU and on the oracle; compare every step."""
     import torch
 
-    g = GpuShard(w, n=n, spill=spill, bias_correction=bias_correction)
+    g = GpuShard(w, n=n, spill=spill, bias_correction=bias_correction, **shard_kw)
     g.init_state()
     ow = OracleWindow(w, 0, n, bias_correction=bias_correction)
     for s in range(1, steps + 1):
@@ -104,6 +104,28 @@ def test_ragged_shapes(base, n, nd, qb, clip):
     w = _variant(base, n_d=nd, quant_block=qb, max_norm=clip,
                  weight_decay=0.1 if clip else 0.0)
     g, _ = _run_pair(w, n, 3)
+    g.free()
+
+
+@pytest.mark.parametrize("base,n,nd,qb,clip", [
+    ("13B-nd16-clip-int8", 300_001, 16, 256, 1.0),  # spill, clipped update, int8 out
+    ("7.5B-nd64", 20_000 + 4, 64, 0, 0.0),          # wide update over the rows
+    ("13B-nd1-stage0", 100_003, 1, 0, 0.0),         # one row, one-chunk update
+])
+def test_spaced_layout_against_oracle(base, n, nd, qb, clip):
+    """The caller's arrays in the spaced layout (one arena, each array at the
+    start of its own slot, as `bench.py --layout spaced` places them; slots
+    of 64 MiB here) against the oracle at every step: only the addresses
+    differ from the one-allocation-per-array layout."""
+    log(f"case spaced layout {base} n={n} n_d={nd} block={qb} clip={clip}")
+    w = _variant(base, n_d=nd, quant_block=qb, max_norm=clip,
+                 weight_decay=0.1 if clip else 0.0)
+    g, _ = _run_pair(w, n, 3, layout="spaced", slot_bytes=64 << 20)
+    assert g.arena is not None
+    base_ptr = g.arena.data_ptr()
+    for k, a in enumerate(x for x in (g.master, g.m, g.v, g.p, g.codes, g.scales, g.gbar_ws)
+                          if x is not None):
+        assert a.data_ptr() == base_ptr + k * (64 << 20)
     g.free()
 
 
