@@ -16,8 +16,9 @@
 // the element loop vectorizes to binary64 AVX2, or AVX-512 where the host
 // has it (vdivpd and vsqrtpd are correctly rounded, no contraction, so both
 // give the same bits), and the shard is split over a pool of host threads
-// in contiguous, quantizer-block-aligned ranges.
+// that take contiguous, quantizer-block-aligned chunks in turn.
 
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <cstdlib>
@@ -173,14 +174,20 @@ extern "C" int zero_shard_host_step(const zs_desc *d, const float *gbar, float l
     k.coef = (c != c) ? c : (c < 1.0 ? c : 1.0);
   }
 
-  // contiguous ranges, aligned to the quantizer block so that every block is
-  // quantized by the thread that produced its bf16 values
-  const int64_t align = qb ? qb : 64;
+  // Chunks of kChunk elements (a multiple of every quantizer block, so each
+  // block is quantized by the thread that produced its bf16 values), handed
+  // out in order from a shared counter: a thread that the host deschedules
+  // (the cores are shared with the HIP runtime's copy threads when the
+  // update runs inside the offload pipeline) holds up one chunk, not a
+  // fixed 1/threads of the shard.  Every element's arithmetic is its own,
+  // so the split changes no bit.
+  constexpr int64_t kChunk = int64_t(1) << 18;
+  static_assert(kChunk % 512 == 0, "chunks hold whole quantizer blocks");
+  const int64_t nchunks = (n + kChunk - 1) / kChunk;
   int64_t nt = threads < 1 ? 1 : threads;
   const int64_t min_piece = int64_t(1) << 16;
   if (nt > (n + min_piece - 1) / min_piece) nt = (n + min_piece - 1) / min_piece;
-  int64_t piece = (n + nt - 1) / nt;
-  piece = (piece + align - 1) / align * align;
+  if (nt > nchunks) nt = nchunks;
   const bool wide = have_avx512() && std::getenv("ZS_HOST_NO_AVX512") == nullptr;
   auto work = [&](int64_t lo, int64_t hi) {
     const int64_t b_lo = qb ? lo / qb : 0, b_hi = qb ? (hi + qb - 1) / qb : 0;
@@ -192,12 +199,17 @@ extern "C" int zero_shard_host_step(const zs_desc *d, const float *gbar, float l
       if (qb) quant_blocks_avx2(d->param_out, d->q_codes, d->q_scales, b_lo, b_hi, n, qb);
     }
   };
+  std::atomic<int64_t> next{0};
+  auto run = [&]() {
+    for (int64_t c = next.fetch_add(1, std::memory_order_relaxed); c < nchunks;
+         c = next.fetch_add(1, std::memory_order_relaxed)) {
+      const int64_t lo = c * kChunk;
+      work(lo, lo + kChunk < n ? lo + kChunk : n);
+    }
+  };
   std::vector<std::thread> pool;
-  for (int64_t lo = piece; lo < n; lo += piece) {
-    const int64_t hi = lo + piece < n ? lo + piece : n;
-    pool.emplace_back(work, lo, hi);
-  }
-  work(0, piece < n ? piece : n);
+  for (int64_t i = 1; i < nt; ++i) pool.emplace_back(run);
+  run();
   for (auto &th : pool) th.join();
   return ZS_OK;
 }
