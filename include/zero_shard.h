@@ -296,7 +296,8 @@ int zero_shard_dequant(const int8_t *const *codes, const float *const *scales, i
  * zero_shard_gnorm wrote, copied to the host.  global_sumsq is S, used iff
  * d->max_norm > 0.  The arithmetic is the device step's, so the result is
  * bit-identical to zero_shard_step on the same inputs.  Synchronous; runs
- * on `threads` host threads (>= 1) over contiguous, block-aligned ranges.
+ * on `threads` host threads (>= 1), which take contiguous 2^18-element,
+ * block-aligned pieces of the shard in turn (the split changes no bit).
  * Errors: ZS_EINVAL. */
 int zero_shard_host_step(const zs_desc *d, const float *gbar, float lr, int64_t t,
                          double global_sumsq, int32_t threads);
@@ -312,17 +313,19 @@ int zero_shard_host_step(const zs_desc *d, const float *gbar, float lr, int64_t 
  * aligned) that the updated parameters are uploaded into, alternately;
  * `stream` is the caller's compute stream; `threads` (>= 1) host threads
  * run the update.  The library allocates a device spill and S scalar, two
- * pinned gradient slots and two pinned bf16 slots, and a download and an
- * upload stream.
+ * pinned gradient slots and two pinned bf16 slots, a download and an
+ * upload stream, and one event per 2^24-element chunk of each gradient slot.
  *
  * zero_shard_offload_step: step t.  Queues on `stream` the norm pass over
  * contrib (a HOST array of n_d device pointers, as for zero_shard_gnorm),
- * then copies the averaged gradient and S_local to pinned memory, waits
- * for the host update of the previous step to finish, orders `stream`
- * after that step's upload, starts this step's host update (a3-a5 with
- * S = S_local + s_other, s_other >= 0 being the other shards' sum) on a
- * host thread, and returns.  The host update uploads its bf16 parameters
- * into buffer (call index mod 2).  Work queued on `stream` after the call
+ * then copies S_local and the averaged gradient to pinned memory (the
+ * gradient in chunks of 2^24 elements), waits for the host update of the
+ * previous step to finish, orders `stream` after that step's upload, starts
+ * this step's host update (a3-a5 with S = S_local + s_other, s_other >= 0
+ * being the other shards' sum) on a host thread, and returns.  The host
+ * update takes each chunk as soon as its copy has landed and uploads each
+ * chunk of its bf16 parameters into buffer (call index mod 2) as soon as
+ * it is written.  Work queued on `stream` after the call
  * sees the parameters of the previous step: zero_shard_offload_params
  * names that buffer (NULL before any update has been uploaded).
  * zero_shard_offload_wait: finish the running host update and order

@@ -24,11 +24,14 @@
 #include <cstdlib>
 #include <cstring>
 #include <limits>
+#include <memory>
+#include <new>
 #include <thread>
 #include <vector>
 
 #include "zero_shard.h"
 #include "zs_args.h"
+#include "zs_host.h"
 
 namespace {
 
@@ -146,8 +149,8 @@ extern "C" int64_t zero_shard_len(int64_t phi, int32_t n_d, int32_t r) {
   return rest < per ? rest : per;
 }
 
-extern "C" int zero_shard_host_step(const zs_desc *d, const float *gbar, float lr, int64_t t,
-                                    double global_sumsq, int32_t threads) {
+int zs_host::step(const zs_desc *d, const float *gbar, float lr, int64_t t, double global_sumsq,
+                  int32_t threads, const Hooks *hooks) {
   if (!d) return ZS_EINVAL;
   if (!zs_args::geometry_ok(*d) || !zs_args::hyper_ok(*d) || !zs_args::step_ok(lr, t))
     return ZS_EINVAL;
@@ -199,17 +202,49 @@ extern "C" int zero_shard_host_step(const zs_desc *d, const float *gbar, float l
       if (qb) quant_blocks_avx2(d->param_out, d->q_codes, d->q_scales, b_lo, b_hi, n, qb);
     }
   };
+  // with hooks: hook chunk h covers update chunks [h*per, (h+1)*per); left[h]
+  // counts its update chunks still to finish, and the thread that finishes
+  // the last one reports it
+  const int64_t per = hooks ? hooks->chunk / kChunk : 1;
+  const int64_t nhook = hooks ? (nchunks + per - 1) / per : 0;
+  std::unique_ptr<std::atomic<int64_t>[]> left;
+  if (hooks) {
+    if (hooks->chunk < kChunk || hooks->chunk % kChunk) return ZS_EINVAL;
+    left.reset(new (std::nothrow) std::atomic<int64_t>[nhook]);
+    if (!left) return ZS_ENOMEM;
+    for (int64_t h = 0; h < nhook; ++h)
+      left[h].store(nchunks - h * per < per ? nchunks - h * per : per, std::memory_order_relaxed);
+  }
   std::atomic<int64_t> next{0};
+  std::atomic<int> failed{0};
   auto run = [&]() {
-    for (int64_t c = next.fetch_add(1, std::memory_order_relaxed); c < nchunks;
+    int64_t seen = -1;  // the last hook chunk this thread saw ready (chunks come in order)
+    for (int64_t c = next.fetch_add(1, std::memory_order_relaxed);
+         c < nchunks && !failed.load(std::memory_order_relaxed);
          c = next.fetch_add(1, std::memory_order_relaxed)) {
+      const int64_t h = c / per;
+      if (hooks && h > seen) {
+        if (hooks->ready(hooks->ctx, h)) {
+          failed.store(1);
+          break;
+        }
+        seen = h;
+      }
       const int64_t lo = c * kChunk;
       work(lo, lo + kChunk < n ? lo + kChunk : n);
+      if (hooks && left[h].fetch_sub(1, std::memory_order_acq_rel) == 1 &&
+          hooks->done(hooks->ctx, h))
+        failed.store(1);
     }
   };
   std::vector<std::thread> pool;
   for (int64_t i = 1; i < nt; ++i) pool.emplace_back(run);
   run();
   for (auto &th : pool) th.join();
-  return ZS_OK;
+  return failed.load() ? ZS_EHIP : ZS_OK;
+}
+
+extern "C" int zero_shard_host_step(const zs_desc *d, const float *gbar, float lr, int64_t t,
+                                    double global_sumsq, int32_t threads) {
+  return zs_host::step(d, gbar, lr, t, global_sumsq, threads, nullptr);
 }

@@ -7,11 +7,20 @@
 //
 //   GPU, caller's stream   norm pass of step s (averaged gradient -> the
 //                          device spill, S_local -> a device scalar)
-//   download stream        spill and S_local -> pinned host slot s mod 2
-//   host worker thread     wait for the copy; a3-a5 over the host-resident
-//                          fp32 state (zero_shard_host_step) into pinned
-//                          bf16 slot s mod 2; upload it (upload stream)
-//                          into device parameter buffer s mod 2
+//   download stream        S_local, then the spill in chunks of 2^24
+//                          elements -> pinned host slot s mod 2, an event
+//                          after each chunk
+//   host worker thread     a3-a5 over the host-resident fp32 state (the
+//                          update of zero_shard_host_step) into pinned bf16
+//                          slot s mod 2, each chunk as soon as its download
+//                          has landed; each chunk's bf16 uploaded (upload
+//                          stream) into device parameter buffer s mod 2 as
+//                          soon as it is written
+//
+// The chunks stream the download, the update and the upload through one
+// another: the update of step s starts when the first chunk of its gradient
+// has arrived instead of the whole spill, and its parameters are on the
+// device a chunk after the update ends.
 //
 // The call for step s returns once the GPU work is queued and the host
 // update of step s-1 has finished; the host update of step s then runs
@@ -36,6 +45,7 @@
 
 #include "zero_shard.h"
 #include "zs_args.h"
+#include "zs_host.h"
 
 struct zs_offload {
   uint32_t magic;
@@ -54,6 +64,9 @@ struct zs_offload {
   zs_bf16 *p_host[2];    // pinned
   hipEvent_t normed;     // the norm pass of the current step is done
   hipEvent_t copied[2], uploaded[2];
+  hipEvent_t s_copied[2];     // S_local of slot k is in host memory
+  hipEvent_t *chunk_copied[2]; // spill chunk h of slot k is in host memory
+  int64_t nio;                 // spill chunks of kIoChunk elements
   std::thread worker;
   int worker_rc;
   int64_t steps;         // steps queued so far
@@ -63,6 +76,10 @@ struct zs_offload {
 namespace {
 
 constexpr uint32_t kOffloadMagic = 0x5a534f31u;
+// Elements per streamed chunk of the download and the upload (64 MiB of the
+// fp32 spill, about a millisecond of PCIe): a multiple of the host update's
+// work unit.
+constexpr int64_t kIoChunk = int64_t(1) << 24;
 
 std::mutex g_mu;
 std::unordered_set<zs_offload *> g_live;
@@ -86,6 +103,12 @@ void release(zs_offload *o) {
     if (o->p_host[k]) (void)hipHostFree(o->p_host[k]);
     if (o->copied[k]) (void)hipEventDestroy(o->copied[k]);
     if (o->uploaded[k]) (void)hipEventDestroy(o->uploaded[k]);
+    if (o->s_copied[k]) (void)hipEventDestroy(o->s_copied[k]);
+    if (o->chunk_copied[k]) {
+      for (int64_t h = 0; h < o->nio; ++h)
+        if (o->chunk_copied[k][h]) (void)hipEventDestroy(o->chunk_copied[k][h]);
+      delete[] o->chunk_copied[k];
+    }
   }
   if (o->normed) (void)hipEventDestroy(o->normed);
   if (o->dev) (void)zero_shard_free(o->dev);
@@ -95,23 +118,51 @@ void release(zs_offload *o) {
   if (o->sumsq_dev) (void)hipFree(o->sumsq_dev);
 }
 
+struct Slot {
+  zs_offload *o;
+  int k;
+};
+
+int64_t io_len(const zs_offload *o, int64_t h) {
+  const int64_t lo = h * kIoChunk;
+  return o->n - lo < kIoChunk ? o->n - lo : kIoChunk;
+}
+
+// Hooks of the host update (called from its threads): wait for spill chunk
+// h of the slot to land; queue the upload of the slot's bf16 chunk h.
+int chunk_ready(void *ctx, int64_t h) {
+  const Slot *s = static_cast<const Slot *>(ctx);
+  return hipSetDevice(s->o->device) != hipSuccess ||
+         hipEventSynchronize(s->o->chunk_copied[s->k][h]) != hipSuccess;
+}
+
+int chunk_done(void *ctx, int64_t h) {
+  const Slot *s = static_cast<const Slot *>(ctx);
+  const int64_t lo = h * kIoChunk;
+  return hipSetDevice(s->o->device) != hipSuccess ||
+         hipMemcpyAsync(s->o->param_dev[s->k] + lo, s->o->p_host[s->k] + lo,
+                        size_t(io_len(s->o, h)) * 2, hipMemcpyHostToDevice,
+                        s->o->up) != hipSuccess;
+}
+
 // The host half of step t from slot k: run on the worker thread.
 void host_half(zs_offload *o, int k, float lr, int64_t t, double s_other) {
   int rc = ZS_OK;
-  if (hipSetDevice(o->device) != hipSuccess || hipEventSynchronize(o->copied[k]) != hipSuccess ||
+  // S_local has landed, and the upload that last read bf16 slot k is done
+  if (hipSetDevice(o->device) != hipSuccess || hipEventSynchronize(o->s_copied[k]) != hipSuccess ||
       hipEventSynchronize(o->uploaded[k]) != hipSuccess) {
     o->worker_rc = ZS_EHIP;
     return;
   }
   zs_desc h = o->host;
   h.param_out = o->p_host[k];
-  rc = zero_shard_host_step(&h, o->gbar_host[k], lr, t, *o->s_host[k] + s_other, o->threads);
-  if (rc == ZS_OK && o->n > 0) {
-    if (hipMemcpyAsync(o->param_dev[k], o->p_host[k], size_t(o->n) * 2, hipMemcpyHostToDevice,
-                       o->up) != hipSuccess ||
-        hipEventRecord(o->uploaded[k], o->up) != hipSuccess)
-      rc = ZS_EHIP;
-  }
+  Slot slot{o, k};
+  const zs_host::Hooks hooks{kIoChunk, &slot, chunk_ready, chunk_done};
+  rc = zs_host::step(&h, o->gbar_host[k], lr, t, *o->s_host[k] + s_other, o->threads,
+                     o->n > 0 ? &hooks : nullptr);
+  // every chunk's upload is queued: the event marks the last of them
+  if (rc == ZS_OK && o->n > 0 && hipEventRecord(o->uploaded[k], o->up) != hipSuccess)
+    rc = ZS_EHIP;
   o->worker_rc = rc;
 }
 
@@ -160,8 +211,20 @@ int zero_shard_offload_init(const zs_desc *host, zs_bf16 *param_dev0, zs_bf16 *p
         hipHostMalloc(&o->p_host[k], nb * 2, hipHostMallocDefault) != hipSuccess)
       rc = ZS_ENOMEM;
     else if (hipEventCreateWithFlags(&o->copied[k], hipEventDisableTiming) != hipSuccess ||
-             hipEventCreateWithFlags(&o->uploaded[k], hipEventDisableTiming) != hipSuccess)
+             hipEventCreateWithFlags(&o->uploaded[k], hipEventDisableTiming) != hipSuccess ||
+             hipEventCreateWithFlags(&o->s_copied[k], hipEventDisableTiming) != hipSuccess)
       rc = ZS_EHIP;
+  }
+  o->nio = n > 0 ? (n + kIoChunk - 1) / kIoChunk : 0;
+  for (int k = 0; !rc && k < 2; ++k) {
+    o->chunk_copied[k] = new (std::nothrow) hipEvent_t[o->nio > 0 ? o->nio : 1]();
+    if (!o->chunk_copied[k]) {
+      rc = ZS_ENOMEM;
+      break;
+    }
+    for (int64_t h = 0; !rc && h < o->nio; ++h)
+      if (hipEventCreateWithFlags(&o->chunk_copied[k][h], hipEventDisableTiming) != hipSuccess)
+        rc = ZS_EHIP;
   }
   if (!rc) {
     // the device side: a norm-only handle (no state on the GPU) over the spill
@@ -202,12 +265,19 @@ int zero_shard_offload_step(zs_offload *o, const zs_bf16 *const *contrib, float 
   if (hipEventRecord(o->normed, o->compute) != hipSuccess ||
       hipStreamWaitEvent(o->down, o->normed, 0) != hipSuccess)
     return ZS_EHIP;
-  if (o->n > 0 && hipMemcpyAsync(o->gbar_host[k], o->gbar_ws, size_t(o->n) * 4,
-                                 hipMemcpyDeviceToHost, o->down) != hipSuccess)
-    return ZS_EHIP;
+  // S_local first (the update needs it before any chunk), then the spill
+  // chunk by chunk, an event after each
   if (hipMemcpyAsync(o->s_host[k], o->sumsq_dev, 8, hipMemcpyDeviceToHost, o->down) != hipSuccess ||
-      hipEventRecord(o->copied[k], o->down) != hipSuccess)
+      hipEventRecord(o->s_copied[k], o->down) != hipSuccess)
     return ZS_EHIP;
+  for (int64_t h = 0; h < o->nio; ++h) {
+    const int64_t lo = h * kIoChunk;
+    if (hipMemcpyAsync(o->gbar_host[k] + lo, o->gbar_ws + lo, size_t(io_len(o, h)) * 4,
+                       hipMemcpyDeviceToHost, o->down) != hipSuccess ||
+        hipEventRecord(o->chunk_copied[k][h], o->down) != hipSuccess)
+      return ZS_EHIP;
+  }
+  if (hipEventRecord(o->copied[k], o->down) != hipSuccess) return ZS_EHIP;
   // the host update of the previous step has finished (its state is the
   // input of this one) and its upload is queued: the caller's stream reads
   // those parameters from here on

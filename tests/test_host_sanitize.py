@@ -30,6 +30,7 @@ def test_host_code_under_sanitizers(tmp_path, sanitize, isa):
            "-fno-sanitize-recover=all", "-fno-omit-frame-pointer", "-ffp-contract=off",
            "-fno-fast-math", "-march=x86-64-v3", "-pthread",
            "-I" + os.path.join(ROOT, "include"), "-I" + os.path.join(ROOT, "oracle"),
+           "-I" + os.path.join(ROOT, "sharded_mixed_precision_zero_amd", "csrc"),
            *SRC, "-o", exe]
     subprocess.run(cmd, check=True, capture_output=True, text=True, timeout=300)
     env = dict(os.environ)
