@@ -475,17 +475,19 @@ def test_dequant_roundtrips_the_fused_quantizer():
     g.free()
 
 
-@pytest.mark.parametrize("delayed", [False, True])
-def test_offload_equals_on_device_step(delayed):
+@pytest.mark.parametrize("delayed,n", [(False, 300_001), (True, 300_001),
+                                       (True, (1 << 24) + 4099)])
+def test_offload_equals_on_device_step(delayed, n):
     """ZeRO-Offload (norm on the GPU, state and update on host threads, bf16
     uploaded back), serial or with the one-step delayed update, gives the
-    same bits as the on-device step: same definition, same inputs."""
+    same bits as the on-device step: same definition, same inputs.  The
+    pipeline streams its copies in chunks of 2^24 elements: the last case
+    is two chunks, the second ragged."""
     import torch
 
     from tests._gpu import OffloadShard
 
     w = _variant("13B-nd16-clip-int8", max_norm=0.05)
-    n = 300_001
     log(f"case offload n={n} delayed={delayed}")
     g = GpuShard(w, n=n)
     g.init_state()
