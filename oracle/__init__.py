@@ -21,7 +21,9 @@ from dataclasses import dataclass
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libzsoracle.so")
+# ZS_ORACLE_LIB names another build of zs_oracle.cpp (the mutation test
+# runs the pins against builds with planted mistakes).
+LIB_PATH = os.environ.get("ZS_ORACLE_LIB") or os.path.join(_HERE, "libzsoracle.so")
 
 _c_f64 = ctypes.c_double
 _c_i32 = ctypes.c_int32

@@ -73,7 +73,7 @@ def test_memory_model_limits_and_consistency():
 def test_bf16_round_exhaustive():
     """All 2^32 binary32 patterns against a nearest-neighbour definition."""
     src = os.path.join(ROOT, "tests", "native", "bf16_exhaustive.c")
-    so = os.path.join(ROOT, "oracle", "libzsoracle.so")
+    so = O.LIB_PATH
     with tempfile.TemporaryDirectory() as d:
         exe = os.path.join(d, "bf16ex")
         subprocess.run(["gcc", "-O2", src, so, f"-Wl,-rpath,{os.path.dirname(so)}", "-lm",
