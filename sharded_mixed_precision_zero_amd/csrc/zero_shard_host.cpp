@@ -238,7 +238,13 @@ int zs_host::step(const zs_desc *d, const float *gbar, float lr, int64_t t, doub
     }
   };
   std::vector<std::thread> pool;
-  for (int64_t i = 1; i < nt; ++i) pool.emplace_back(run);
+  for (int64_t i = 1; i < nt; ++i) {
+    try {
+      pool.emplace_back(run);
+    } catch (...) {  // no thread to be had: the running ones take its chunks
+      break;
+    }
+  }
   run();
   for (auto &th : pool) th.join();
   return failed.load() ? ZS_EHIP : ZS_OK;
